@@ -1,0 +1,278 @@
+/*
+ * oracle.c -- plain, slow, single-threaded float64 CPU reference for the
+ * batched speculative-decoding verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header,
+ * table or helper with the GPU path; both sides only see the same seeded
+ * inputs.
+ *
+ * Pages cited (by title and section):
+ *   [A] "推测解码与连续批处理深度实战：突破自回归生成的双重瓶颈"
+ *       (ybb.press llm-inference), section 1.2 (数学原理) and 1.3.
+ *   [B] the blog.hotdry.top post on speculative decoding and dynamic
+ *       batching, part "推测解码：算法层的并行验证艺术", item 流程编排.
+ *   [C] "LLM推理服务的推测解码与PagedAttention内存管理", the flow under
+ *       推测解码（Speculative Decoding）原理.
+ *   [D] "大模型推理加速新范式：推测解码（Speculative Decoding）原理剖析与
+ *       vLLM生产级实现", sections 2.1 and 2.2.
+ *
+ * What is computed, for every sequence b with gamma = gamma_b drafts, in the
+ * pages' order:
+ *   1. The target scores all gamma+1 positions at once ([A] 1.2 step 2,
+ *      [C] step 2): for every target row i in [0, gamma] and draft row i in
+ *      [0, gamma) the distribution softmax(l / T):
+ *        z_k = l_k / T,  M = max_k z_k,  s = sum_k exp(z_k - M) (left to right),
+ *        p_k = exp(z_k - M) / s.
+ *      The pages never define T (only an API field temperature=0.7 appears in
+ *      [D] 4.2); the reading taken is the usual one, the same scalar T > 0
+ *      divides the target and the draft logits.
+ *   2. Accept test, positions in order ([A] 1.2 step 3, [C] step 3, [D] 2.2):
+ *      draft token x_i is accepted with probability min(1, p_i(x)/q_i(x)).
+ *      With the pre-drawn uniform u_i in [0, 1): accept iff u_i < r_i where
+ *      r_i = p_i(x_i) / q_i(x_i) (strict, so r_i >= 1 always accepts).
+ *   3. Stop at the first rejection and drop every later draft ([D] 2.1,
+ *      [B] 流程编排).  n_b = the index j of the first rejection, or gamma.
+ *   4. Final draw with the last uniform of the sequence:
+ *        j < gamma : from norm(max(0, p_j - q_j)) ([A] 1.2 step 3 writes it
+ *                    clip(p_i - q_i, 0); [D] 2.2 writes norm(max(0, p - q)));
+ *        j = gamma : the bonus token, from p_gamma, the target's (gamma+1)-th
+ *                    distribution (implied by the gamma+1 scored positions of
+ *                    [A] 1.2 step 2 and the gamma+1 exponent of [A] 1.3 /
+ *                    [C]'s expected-speed-up formula).
+ *      Inverse CDF over ascending token id: w_k the weights, C_k their
+ *      running sum left to right, S = C_{V-1}, t = u * S, and the token is the
+ *      smallest k with C_k > t (never a zero-weight token).  If rounding
+ *      leaves t >= C_{V-1}, the last k with w_k > 0.  S = 0 cannot occur for
+ *      valid inputs (a rejection needs q_j(x) > p_j(x)); if it does, the draw
+ *      falls back to p_j and the sequence is flagged.
+ *   5. Output: out[i] = x_i for i < n_b, out[n_b] = the drawn token, and
+ *      out[i] = -1 for n_b < i <= gamma, at the sequence's target-row slots.
+ *
+ * Diagnostics: the distance |u_i - r_i| of every evaluated test, and for the
+ * final draw min(t - C_{k-1}, C_k - t) / S; a sequence is flagged when any of
+ * them is below `tie_tol` (the caller passes 1e-6).
+ *
+ * Layout: packed ragged rows, cu[b] = sum of gamma_{b'} for b' < b; target
+ * row of (b, i) is cu[b] + b + i, draft row is cu[b] + i; one uniform per
+ * target row (gamma_b tests, then the final draw).  Logits are f32 (dtype 0)
+ * or bf16 bit patterns (dtype 1); both are widened exactly to double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL -1
+#define ORACLE_ENOMEM -2
+
+/* Exact widening of one stored logit to double. */
+static double load_logit(const void *base, int dtype, int64_t idx) {
+  if (dtype == 0) return (double)((const float *)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Step 1 for one row: M = max_k l_k / T and s = sum_k exp(l_k / T - M). */
+static void row_normaliser(const void *base, int dtype, int64_t row,
+                           int64_t ld, int64_t vocab, double T,
+                           double *M_out, double *s_out) {
+  const int64_t off = row * ld;
+  double M = -INFINITY;
+  for (int64_t k = 0; k < vocab; ++k) {
+    double z = load_logit(base, dtype, off + k) / T;
+    if (z > M) M = z;
+  }
+  double s = 0.0;
+  for (int64_t k = 0; k < vocab; ++k) {
+    double z = load_logit(base, dtype, off + k) / T;
+    s += exp(z - M);
+  }
+  *M_out = M;
+  *s_out = s;
+}
+
+/* p_k of one row, given its normaliser. */
+static double prob(const void *base, int dtype, int64_t row, int64_t ld,
+                   int64_t k, double T, double M, double s) {
+  return exp(load_logit(base, dtype, row * ld + k) / T - M) / s;
+}
+
+/* softmax(l / T) of one row into p[0..vocab). */
+int oracle_row_softmax(const void *logits, int dtype, int64_t vocab,
+                       float temperature, double *p) {
+  if (!logits || !p || vocab <= 0 || !(temperature > 0.0f)) return ORACLE_EINVAL;
+  double M, s;
+  const double T = (double)temperature;
+  row_normaliser(logits, dtype, 0, vocab, vocab, T, &M, &s);
+  for (int64_t k = 0; k < vocab; ++k) p[k] = prob(logits, dtype, 0, vocab, k, T, M, s);
+  return ORACLE_OK;
+}
+
+/* sum_k min(p_k, q_k) for one target row and one draft row: the probability
+ * that a draft token drawn from q passes the accept test. */
+double oracle_overlap_mass(const void *target_row, const void *draft_row,
+                           int dtype, int64_t vocab, float temperature) {
+  double Mp, sp, Mq, sq;
+  const double T = (double)temperature;
+  row_normaliser(target_row, dtype, 0, vocab, vocab, T, &Mp, &sp);
+  row_normaliser(draft_row, dtype, 0, vocab, vocab, T, &Mq, &sq);
+  double a = 0.0;
+  for (int64_t k = 0; k < vocab; ++k) {
+    double p = prob(target_row, dtype, 0, vocab, k, T, Mp, sp);
+    double q = prob(draft_row, dtype, 0, vocab, k, T, Mq, sq);
+    a += p < q ? p : q;
+  }
+  return a;
+}
+
+/*
+ * The whole verify step.  Outputs (all caller-owned, host memory):
+ *   out_tokens[R_t]          int32, n_b + 1 tokens per sequence then -1
+ *   out_num_accepted[B]      int32, n_b in [0, gamma_b]
+ *   out_p_draft, out_q_draft [R_d] double p_i(x_i), q_i(x_i) (may be NULL)
+ *   out_residual_sum[B]      double S of norm(max(0, p - q)), 0 on the bonus
+ *                            path (may be NULL)
+ *   tie_accept[R_d]          double |u_i - r_i|, NaN for tests not evaluated
+ *                            (may be NULL)
+ *   tie_final[B]             double final-draw boundary distance (may be NULL)
+ *   flagged[B]               int32 bit0: an accept test within tie_tol,
+ *                            bit1: the final draw within tie_tol,
+ *                            bit2: empty residual fallback (may be NULL)
+ * Returns 0, or a negative code for invalid arguments / allocation failure.
+ */
+int oracle_verify(int32_t num_seqs, const int32_t *cu_draft,
+                  const void *target_logits, const void *draft_logits,
+                  int64_t ld, int64_t vocab, int dtype,
+                  const int32_t *draft_tokens, const float *uniforms,
+                  float temperature, double tie_tol,
+                  int32_t *out_tokens, int32_t *out_num_accepted,
+                  double *out_p_draft, double *out_q_draft,
+                  double *out_residual_sum, double *tie_accept,
+                  double *tie_final, int32_t *flagged) {
+  if (num_seqs < 0 || vocab <= 0 || ld < vocab || (dtype != 0 && dtype != 1) ||
+      !(temperature > 0.0f) || !isfinite(temperature))
+    return ORACLE_EINVAL;
+  if (num_seqs == 0) return ORACLE_OK;
+  if (!cu_draft || !target_logits || !uniforms || !out_tokens || !out_num_accepted)
+    return ORACLE_EINVAL;
+  const double T = (double)temperature;
+
+  int64_t max_gamma = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    int64_t g = (int64_t)cu_draft[b + 1] - cu_draft[b];
+    if (g < 0) return ORACLE_EINVAL;
+    if (g > max_gamma) max_gamma = g;
+  }
+  if (max_gamma > 0 && (!draft_logits || !draft_tokens)) return ORACLE_EINVAL;
+
+  double *Mp = malloc(sizeof(double) * (size_t)(max_gamma + 1));
+  double *sp = malloc(sizeof(double) * (size_t)(max_gamma + 1));
+  double *Mq = malloc(sizeof(double) * (size_t)(max_gamma + 1));
+  double *sq = malloc(sizeof(double) * (size_t)(max_gamma + 1));
+  double *w = malloc(sizeof(double) * (size_t)vocab);
+  double *C = malloc(sizeof(double) * (size_t)vocab);
+  if (!Mp || !sp || !Mq || !sq || !w || !C) {
+    free(Mp); free(sp); free(Mq); free(sq); free(w); free(C);
+    return ORACLE_ENOMEM;
+  }
+
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t gamma = (int64_t)cu_draft[b + 1] - cu_draft[b];
+    const int64_t trow0 = (int64_t)cu_draft[b] + b; /* target row of (b, 0) */
+    const int64_t drow0 = (int64_t)cu_draft[b];     /* draft row of (b, 0) */
+    int32_t flag = 0;
+
+    /* 1. normalisers of all gamma+1 target rows and gamma draft rows. */
+    for (int64_t i = 0; i <= gamma; ++i)
+      row_normaliser(target_logits, dtype, trow0 + i, ld, vocab, T, &Mp[i], &sp[i]);
+    for (int64_t i = 0; i < gamma; ++i)
+      row_normaliser(draft_logits, dtype, drow0 + i, ld, vocab, T, &Mq[i], &sq[i]);
+
+    /* p_i(x_i), q_i(x_i) for every draft position (reported for all i). */
+    for (int64_t i = 0; i < gamma; ++i) {
+      const int64_t x = draft_tokens[drow0 + i];
+      double p = 0.0, q = 0.0;
+      if (x >= 0 && x < vocab) {
+        p = prob(target_logits, dtype, trow0 + i, ld, x, T, Mp[i], sp[i]);
+        q = prob(draft_logits, dtype, drow0 + i, ld, x, T, Mq[i], sq[i]);
+      }
+      if (out_p_draft) out_p_draft[drow0 + i] = p;
+      if (out_q_draft) out_q_draft[drow0 + i] = q;
+      if (tie_accept) tie_accept[drow0 + i] = NAN;
+    }
+
+    /* 2-3. accept tests in position order, stop at the first rejection. */
+    int64_t j = gamma;
+    for (int64_t i = 0; i < gamma; ++i) {
+      const int64_t x = draft_tokens[drow0 + i];
+      if (x < 0 || x >= vocab) { free(Mp); free(sp); free(Mq); free(sq); free(w); free(C); return ORACLE_EINVAL; }
+      const double p = prob(target_logits, dtype, trow0 + i, ld, x, T, Mp[i], sp[i]);
+      const double q = prob(draft_logits, dtype, drow0 + i, ld, x, T, Mq[i], sq[i]);
+      const double r = p / q;
+      const double u = (double)uniforms[trow0 + i];
+      const double d = fabs(u - r);
+      if (tie_accept) tie_accept[drow0 + i] = d;
+      if (d < tie_tol) flag |= 1;
+      if (!(u < r)) { j = i; break; }
+    }
+
+    /* 4. final draw weights: residual at j, or the bonus distribution. */
+    const int64_t tj = trow0 + j;
+    for (int64_t k = 0; k < vocab; ++k) {
+      const double p = prob(target_logits, dtype, tj, ld, k, T, Mp[j], sp[j]);
+      if (j < gamma) {
+        const double q = prob(draft_logits, dtype, drow0 + j, ld, k, T, Mq[j], sq[j]);
+        w[k] = p - q > 0.0 ? p - q : 0.0;
+      } else {
+        w[k] = p;
+      }
+    }
+    double S = 0.0;
+    for (int64_t k = 0; k < vocab; ++k) { S += w[k]; C[k] = S; }
+    const double S_reported = (j < gamma) ? S : 0.0;
+    if (!(S > 0.0)) { /* empty residual: draw from p_j instead */
+      flag |= 4;
+      S = 0.0;
+      for (int64_t k = 0; k < vocab; ++k) {
+        w[k] = prob(target_logits, dtype, tj, ld, k, T, Mp[j], sp[j]);
+        S += w[k];
+        C[k] = S;
+      }
+    }
+    const double u = (double)uniforms[trow0 + gamma];
+    const double t = u * S;
+    int64_t tok = -1;
+    for (int64_t k = 0; k < vocab; ++k)
+      if (C[k] > t) { tok = k; break; }
+    if (tok < 0)
+      for (int64_t k = vocab - 1; k >= 0; --k)
+        if (w[k] > 0.0) { tok = k; break; }
+    double df = 0.0;
+    if (tok >= 0) {
+      const double lo = tok > 0 ? C[tok - 1] : 0.0;
+      const double hi = C[tok];
+      df = fmin(t - lo, hi - t) / S;
+      if (df < 0.0) df = 0.0;
+    }
+    if (df < tie_tol) flag |= 2;
+
+    /* 5. outputs at the sequence's target-row slots. */
+    for (int64_t i = 0; i <= gamma; ++i) {
+      int32_t v;
+      if (i < j) v = draft_tokens[drow0 + i];
+      else if (i == j) v = (int32_t)tok;
+      else v = -1;
+      out_tokens[trow0 + i] = v;
+    }
+    out_num_accepted[b] = (int32_t)j;
+    if (out_residual_sum) out_residual_sum[b] = S_reported;
+    if (tie_final) tie_final[b] = df;
+    if (flagged) flagged[b] = flag;
+  }
+  free(Mp); free(sp); free(Mq); free(sq); free(w); free(C);
+  return ORACLE_OK;
+}
