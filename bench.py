@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched speculative-decoding verify step on one MI355X.
+
+One step = one spec_verify_run call (row statistics of every target and draft
+row, accept tests, first-rejection stop, residual / bonus draw) over one batch
+of the headline workload: B=128 sequences, gamma=8, V=128256, bf16 logits,
+T=1.0, heavy-tailed target logits with draft noise giving alpha ~ 0.6.
+Inputs are resident in HBM before timing; `--sets` copies rotate so no step
+reads logits the previous step left in the 256 MB Infinity Cache.
+
+Prints one JSON line: verified rows/s (value), whole-step HBM GB/s, the
+roofline of the dominant kernel (row statistics, HBM-bound, from HIP events
+recorded on the launch stream around every kernel), and the float64 CPU
+oracle timed on this host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "verified rows/s + achieved HBM GB/s (% peak), B=128 γ=8 V=128256 bf16"
+PMC_FILE = os.path.join(ROOT, "profiles", "row_stats_B128_g8_V128256_bf16.pmc.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_08_amd", "csrc", f)
+                  for f in ("spec_verify_kernels.hpp", "spec_verify.hip")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(src_hash: str):
+    """HBM bytes per row-stats launch from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernels changed since."""
+    try:
+        rec = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(inp, num_accepted):
+    """Minimum bytes one step must move: every logit row once, plus the
+    final-draw row(s) once more (2 rows after a rejection, 1 for the bonus),
+    plus tokens, uniforms, offsets and outputs."""
+    import numpy as np
+    e = 2 if inp.dtype == "bf16" else 4
+    V = inp.vocab
+    first = (inp.target_rows + inp.draft_rows) * V * e
+    rejected = int((num_accepted < inp.gammas).sum())
+    reread = (2 * rejected + (inp.num_seqs - rejected)) * V * e
+    small = (inp.draft_rows * 4 + inp.target_rows * 4 + (inp.num_seqs + 1) * 4 +
+             inp.target_rows * 4 + inp.num_seqs * 4 + inp.draft_rows * 8 + inp.num_seqs * 4)
+    return first, reread, small
+
+
+def cpu_baseline(inp, budget_s: float):
+    import oracle
+    oracle._load()
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        oracle.verify_inputs(inp)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 50:
+            break
+    return {"value": inp.target_rows * runs / el, "unit": "verified rows/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the full headline batch ({inp.num_seqs} sequences, {inp.target_rows} "
+                      f"target rows), {runs} run(s) in {el:.1f} s, single-threaded float64 C"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="named workload 1..5")
+    ap.add_argument("--sets", type=int, default=3, help="rotating device input copies")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the verify step shards by sequence with "
+              "no exchange, and this build runs on a single MI355X (use --gpus 1).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import workloads as W
+    from rejection_sampling_verify_08_amd import SpecVerifier
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    t_gen = time.perf_counter()
+    inp = W.config(a.config)
+    print(f"[bench] generated {inp.name} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
+          flush=True)
+    tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+
+    def up(arr):
+        if inp.dtype == "bf16":
+            return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(arr).to(dev)
+
+    host_t, host_d = up(inp.target_logits), up(inp.draft_logits)
+    sets = []
+    for s in range(max(1, a.sets)):
+        t = torch.empty_like(host_t)
+        d = torch.empty_like(host_d)
+        t.copy_(host_t)
+        d.copy_(host_d)
+        sets.append((t, d))
+    del host_t, host_d
+    cu = torch.from_numpy(inp.cu_draft).to(dev)
+    tok = torch.from_numpy(inp.draft_tokens).to(dev)
+    uni = torch.from_numpy(inp.uniforms).to(dev)
+    sv = SpecVerifier(inp.vocab, tdt, max_seqs=inp.num_seqs, max_draft_rows=inp.draft_rows)
+    outs = [sv.allocate_outputs(inp.num_seqs, inp.draft_rows) for _ in sets]
+    nk = sv.num_kernels
+    stream = torch.cuda.current_stream(dev)
+
+    def make_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)          # creates the underlying hipEvent
+        return evs
+
+    for i in range(a.warmup):
+        t, d = sets[i % len(sets)]
+        sv(cu, t, d, tok, uni, inp.temperature, out=outs[i % len(sets)], stream=stream)
+    ev = [make_events(2 * nk) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        t, d = sets[i % len(sets)]
+        sv(cu, t, d, tok, uni, inp.temperature, out=outs[i % len(sets)], stream=stream,
+           timing_events=ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / a.steps
+    k_ms = [[ev[i][2 * k].elapsed_time(ev[i][2 * k + 1]) for i in range(a.steps)]
+            for k in range(nk)]
+    k_avg = [sum(x) / len(x) for x in k_ms]
+
+    num_acc = outs[0].num_accepted.cpu().numpy()
+    status = int(outs[0].status.cpu().item())
+    first, reread, small = algorithmic_bytes(inp, num_acc)
+    step_bytes = first + reread + small
+    value = inp.target_rows / (ms_step / 1e3)
+    hbm = step_bytes / (ms_step / 1e3) / 1e9
+    achieved = first / (k_avg[0] / 1e3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile(src_hash)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic, "kernel": "row_stats_kernel",
+            "kernel_avg_us": round(k_avg[0] * 1e3, 2),
+            "algorithmic_bytes_per_launch": first}
+    cpu = None
+    if a.cpu_budget > 0:
+        cpu = cpu_baseline(inp, a.cpu_budget)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "verified rows/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": inp.name, "B": inp.num_seqs, "gamma": 8 if a.config == 3 else None,
+                   "V": inp.vocab, "logits": inp.dtype, "temperature": inp.temperature,
+                   "accumulate": "f64", "input_sets": len(sets),
+                   "target_rows": inp.target_rows, "draft_rows": inp.draft_rows},
+        "hbm_gbps": round(hbm, 1), "hbm_frac": round(hbm / PEAK_HBM_GBPS, 4),
+        "step_algorithmic_bytes": step_bytes,
+        "kernel_avg_us": [round(x * 1e3, 2) for x in k_avg],
+        "mean_accepted": round(float(num_acc.mean()), 4), "status": status,
+        "roofline": roof, "cpu_baseline": cpu,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(line, ensure_ascii=False), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,205 @@
+/*
+ * spec_verify.h -- C ABI of the batched speculative-decoding verify step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by title and section):
+ *   [A] "推测解码与连续批处理深度实战：突破自回归生成的双重瓶颈", section 1.2:
+ *       a draft model proposes gamma tokens (step 1); the target model scores
+ *       all gamma+1 positions in one parallel pass (step 2); each draft token
+ *       x at position i is accepted with probability min(1, p_i(x) / q_i(x)),
+ *       and a rejected position is resampled from clip(p_i - q_i, 0)
+ *       (step 3); the output then has exactly the target's distribution
+ *       (step 4).
+ *   [D] "大模型推理加速新范式：推测解码（Speculative Decoding）原理剖析与
+ *       vLLM生产级实现", section 2.1 (verification stops at the first
+ *       rejected position and every later draft is dropped) and section 2.2
+ *       (the acceptance ratio min(1, p(x)/q(x)) and the resampling
+ *       distribution norm(max(0, p - q))).
+ *   [B] the blog.hotdry.top post on speculative decoding and dynamic
+ *       batching, items 流程编排 (compare candidates in order, keep the prefix
+ *       before the first mismatch) and 硬件并行 (pack the candidates of many
+ *       requests into one batch), and its 结合使用 paragraph (speculative and
+ *       plain-decode requests share a batch).
+ *   [E] the same vLLM page, section 5.2: requests are rejected at different
+ *       positions, so padded batches waste work -- hence the packed layout.
+ *
+ * Readings where the pages are silent (each one is fixed here):
+ *   - p = softmax(l_target / T), q = softmax(l_draft / T) with one scalar
+ *     temperature T > 0 for both (the pages only show temperature=0.7 as an
+ *     API field, [D] section 4.2).
+ *   - draft i is accepted iff u_i < p_i(x_i) / q_i(x_i) (strict).
+ *   - when all gamma drafts pass, one bonus token is drawn from the target's
+ *     (gamma+1)-th distribution (implied by the gamma+1 scored positions of
+ *     [A] step 2).
+ *   - every draw is an inverse-CDF draw over ascending token id with one
+ *     pre-drawn uniform: the smallest k with C_k > u * S, where C_k is the
+ *     running sum of the weights and S their total.
+ *
+ * Packed ragged layout (no padding), one launch for any mix of gamma_b >= 0
+ * (gamma_b = 0 is a plain decode step: one draw from the target row):
+ *   cu_draft[b]  = gamma_0 + ... + gamma_{b-1}      (int32, B+1 entries)
+ *   target row of (b, i), 0 <= i <= gamma_b :  cu_draft[b] + b + i
+ *   draft row of (b, i),  0 <= i <  gamma_b :  cu_draft[b] + i
+ *   R_d = cu_draft[B] draft rows, R_t = R_d + B target rows
+ *   uniforms[target row of (b, i)], i < gamma_b : accept test of draft i
+ *   uniforms[target row of (b, gamma_b)]        : the final draw (resample
+ *                                                 or bonus)
+ *   out_tokens[target row of (b, i)] : draft i for i < n_b, the drawn token
+ *                                      at i = n_b, -1 for n_b < i <= gamma_b
+ *
+ * Memory, ownership, threading:
+ *   - Every pointer in spec_verify_args is DEVICE memory owned by the caller
+ *     (allocated for example by PyTorch); the library allocates nothing and
+ *     frees nothing.  The context holds only host-side state.
+ *   - spec_verify_run only enqueues kernels on the given HIP stream and never
+ *     synchronises; inputs must stay valid until the stream passes the call.
+ *   - A context is immutable after creation.  Calls on different streams
+ *     may overlap if each uses its own workspace; calls that share a
+ *     workspace must be ordered (same stream).
+ *
+ * Errors: functions return SPEC_VERIFY_OK (0) or a negative status; no C++
+ * exception or abort crosses the ABI.  Argument checks happen on the host
+ * before any HIP call.  Device-data preconditions (monotone cu_draft with
+ * cu_draft[B] = R_d, tokens in [0, V), uniforms in [0, 1), logits finite or
+ * -inf with at least one finite entry per row, q_i(x_i) > 0) are the
+ * caller's.  Out-of-range offsets and tokens never cause out-of-bounds
+ * accesses: the kernels skip such sequences (their outputs become -1) and,
+ * when `status` is given, OR the SPEC_VERIFY_DEV_* bits into it; with
+ * SPEC_VERIFY_FLAG_CHECK the remaining preconditions are checked as well.
+ */
+#ifndef SPEC_VERIFY_H_
+#define SPEC_VERIFY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SPEC_VERIFY_API __attribute__((visibility("default")))
+#else
+#define SPEC_VERIFY_API
+#endif
+
+/* Return codes. */
+#define SPEC_VERIFY_OK 0
+#define SPEC_VERIFY_EINVAL -1      /* NULL required pointer, B < 0, T <= 0 or
+                                      non-finite, ld < V, unaligned element
+                                      pointers, wrong device, bad sizes */
+#define SPEC_VERIFY_EUNSUPPORTED -2 /* dtype not f32/bf16, V <= 0, V > 2^31-1 */
+#define SPEC_VERIFY_ECAPACITY -3   /* B > max_seqs, R_d > max_draft_rows,
+                                      workspace smaller than required */
+#define SPEC_VERIFY_EHIP -4        /* a HIP call failed; see
+                                      spec_verify_last_hip_error() */
+
+/* Logit element types. */
+#define SPEC_VERIFY_F32 0
+#define SPEC_VERIFY_BF16 1
+
+/* Create-time flags. */
+#define SPEC_VERIFY_FLAG_CHECK 1u  /* kernels validate every device-data
+                                      precondition into *status */
+
+/* Bits the kernels OR into *status (when status != NULL). */
+#define SPEC_VERIFY_DEV_BAD_OFFSETS 1u   /* cu_draft not monotone / out of range;
+                                            the sequence is skipped */
+#define SPEC_VERIFY_DEV_BAD_TOKEN 2u     /* a draft token outside [0, V); the
+                                            sequence is skipped */
+#define SPEC_VERIFY_DEV_BAD_UNIFORM 4u   /* (CHECK) a uniform outside [0, 1) */
+#define SPEC_VERIFY_DEV_BAD_LOGIT 8u     /* (CHECK) a NaN or +inf logit */
+#define SPEC_VERIFY_DEV_EMPTY_ROW 16u    /* (CHECK) a row with no finite logit */
+#define SPEC_VERIFY_DEV_ZERO_Q 32u       /* (CHECK) q_i(x_i) = 0 */
+#define SPEC_VERIFY_DEV_EMPTY_RESIDUAL 64u /* the residual summed to 0; the draw
+                                              fell back to p at that position */
+
+typedef struct spec_verify_ctx spec_verify_ctx;
+
+typedef struct {
+  int32_t num_seqs;            /* B >= 0 (host scalar); B = 0 is a no-op */
+  int64_t total_draft_rows;    /* R_d = cu_draft[B] (host scalar) */
+  const int32_t *cu_draft;     /* [B+1] exclusive prefix of gamma_b */
+  const void *target_logits;   /* [R_t rows, pitch ld] of dtype */
+  const void *draft_logits;    /* [R_d rows, pitch ld] of dtype (may be NULL
+                                  when R_d = 0) */
+  int64_t ld;                  /* row pitch in elements, >= V; a 16-byte
+                                  aligned base and pitch take the vector path */
+  const int32_t *draft_tokens; /* [R_d] the proposed tokens, in [0, V) */
+  const float *uniforms;       /* [R_t] pre-drawn U[0,1) values */
+  float temperature;           /* T > 0, applied to target and draft logits */
+  int32_t *out_tokens;         /* [R_t] see the layout above */
+  int32_t *out_num_accepted;   /* [B] n_b in [0, gamma_b] */
+  float *out_p_draft;          /* [R_d] p_i(x_i), optional (NULL = skip) */
+  float *out_q_draft;          /* [R_d] q_i(x_i), optional */
+  float *out_residual_sum;     /* [B] sum_k max(0, p - q) at the rejected
+                                  position, 0 when the bonus was drawn;
+                                  optional */
+  void *workspace;             /* >= spec_verify_workspace_size() bytes,
+                                  256-byte aligned; no initial contents needed */
+  size_t workspace_bytes;
+  uint32_t *status;            /* optional device word; the kernels OR
+                                  SPEC_VERIFY_DEV_* bits into it (the caller
+                                  clears it) */
+  void *const *timing_events;  /* optional: hipEvent_t[2 * kernels] recorded
+                                  on the stream before and after each kernel,
+                                  in launch order (see spec_verify_num_kernels) */
+} spec_verify_args;
+
+/*
+ * Create a context for one device, vocabulary size and logit dtype.
+ * max_seqs / max_draft_rows bound B and R_d of later runs and fix the
+ * workspace size, returned in *workspace_bytes.  The device's properties are
+ * read here (this is the only call that queries the HIP runtime besides
+ * run).  Returns OK, EINVAL, EUNSUPPORTED or EHIP; *out is NULL on failure.
+ */
+SPEC_VERIFY_API int spec_verify_create(spec_verify_ctx **out, int device,
+                                       int64_t vocab, int dtype,
+                                       int32_t max_seqs,
+                                       int64_t max_draft_rows, uint32_t flags,
+                                       size_t *workspace_bytes);
+
+/*
+ * Workspace bytes a context with these bounds needs, without creating one or
+ * touching the HIP runtime (host-only; lets a caller size its allocation
+ * first).  The workspace holds one 16-byte row-statistics partial per 4096
+ * logits of every target and draft row (R_t + R_d = B + 2 R_d rows), one
+ * double per 2048-logit tile of each sequence's final-draw row, and one
+ * arrival counter per sequence.  Returns OK, EINVAL or EUNSUPPORTED.
+ */
+SPEC_VERIFY_API int spec_verify_query_workspace(int64_t vocab, int32_t max_seqs,
+                                                int64_t max_draft_rows,
+                                                size_t *workspace_bytes);
+
+/* Workspace bytes one run with this context needs (same value create gave). */
+SPEC_VERIFY_API size_t spec_verify_workspace_size(const spec_verify_ctx *ctx);
+
+/* Number of kernels one run launches (each bracketed by two timing events). */
+SPEC_VERIFY_API int spec_verify_num_kernels(const spec_verify_ctx *ctx);
+
+/*
+ * Enqueue one verify step on `hip_stream` (a hipStream_t; NULL = the null
+ * stream) on the context's device, which must be the current device.
+ * Computes, for every sequence: p and q at all positions, the accepted count
+ * n_b (first rejection, [D] 2.1), the emitted tokens, and the resampled or
+ * bonus token ([A] 1.2 step 3).  Outputs are written only to the caller's
+ * buffers and the workspace.
+ */
+SPEC_VERIFY_API int spec_verify_run(const spec_verify_ctx *ctx,
+                                    const spec_verify_args *args,
+                                    void *hip_stream);
+
+/* Destroy a context (NULL is accepted).  Returns OK. */
+SPEC_VERIFY_API int spec_verify_destroy(spec_verify_ctx *ctx);
+
+/* Static description of a return code. */
+SPEC_VERIFY_API const char *spec_verify_status_string(int status);
+
+/* The hipError_t of the last EHIP failure on the calling thread (0 if none). */
+SPEC_VERIFY_API int spec_verify_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H_ */

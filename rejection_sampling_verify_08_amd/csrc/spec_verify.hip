@@ -1,0 +1,261 @@
+// spec_verify.hip -- host side of the C ABI declared in include/spec_verify.h:
+// argument checks, workspace layout, and the two launches of one verify step
+// on the caller's HIP stream.  The device code is in spec_verify_kernels.hpp.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "spec_verify.h"
+#include "spec_verify_kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return SPEC_VERIFY_EHIP;
+}
+
+// Workspace sections, in bytes from the workspace base.
+struct Layout {
+  size_t partials = 0;   // Partial[(max_seqs + 2 * max_draft_rows) * tasks_per_row]
+  size_t tiles = 0;      // double[max_seqs * num_tiles]
+  size_t counters = 0;   // uint32[max_seqs]
+  size_t total = 0;
+};
+
+}  // namespace
+
+struct spec_verify_ctx {
+  int device;
+  int64_t vocab;
+  int dtype;
+  int32_t max_seqs;
+  int64_t max_draft_rows;
+  uint32_t flags;
+  int cu_count;
+  int64_t tasks_per_row;   // wave tasks of 4096 elements per row
+  int64_t num_tiles;       // 2048-element tiles per row
+  Layout layout;
+};
+
+namespace {
+
+Layout make_layout(int32_t max_seqs, int64_t max_draft_rows, int64_t tasks_per_row,
+                   int64_t num_tiles) {
+  Layout L;
+  // row statistics cover every target row (R_t = B + R_d) and every draft
+  // row (R_d)
+  const int64_t rows = (int64_t)max_seqs + 2 * max_draft_rows;
+  size_t off = 0;
+  L.partials = off;
+  off = align_up(off + (size_t)rows * (size_t)tasks_per_row * sizeof(sv::Partial));
+  L.tiles = off;
+  off = align_up(off + (size_t)max_seqs * (size_t)num_tiles * sizeof(double));
+  L.counters = off;
+  off = align_up(off + (size_t)max_seqs * sizeof(uint32_t));
+  L.total = off < kAlign ? kAlign : off;
+  return L;
+}
+
+// log2(e)/T split into a float rounded down and a positive float remainder.
+sv::ExpConsts exp_consts(float temperature) {
+  sv::ExpConsts c;
+  const double log2e = 1.4426950408889634074;
+  c.T = (double)temperature;
+  c.c64 = log2e / c.T;
+  float hi = (float)c.c64;
+  if ((double)hi > c.c64) hi = std::nextafter(hi, 0.0f);
+  double lo = c.c64 - (double)hi;
+  if (!(lo > 0.0)) {
+    hi = std::nextafter(hi, 0.0f);
+    lo = c.c64 - (double)hi;
+  }
+  c.c_hi = hi;
+  c.c_lo = (float)lo;
+  return c;
+}
+
+template <int DT, bool VEC, bool CHECK>
+hipError_t launch_all(const spec_verify_ctx* ctx, const spec_verify_args* a,
+                      hipStream_t stream) {
+  using namespace sv;
+  const int64_t B = a->num_seqs;
+  const int64_t R_d = a->total_draft_rows;
+  const int64_t R_t = R_d + B;
+  const int64_t rows = R_t + R_d;
+  const ExpConsts ec = exp_consts(a->temperature);
+  char* ws = static_cast<char*>(a->workspace);
+  Partial* partials = reinterpret_cast<Partial*>(ws + ctx->layout.partials);
+  double* tiles = reinterpret_cast<double*>(ws + ctx->layout.tiles);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + ctx->layout.counters);
+  hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(a->timing_events);
+
+  // kernel 1: one pass over all rows
+  const int64_t wave_tasks = rows * ctx->tasks_per_row;
+  const int64_t grid1 = ceil_div(wave_tasks, kWaves);
+  if (ev) {
+    hipError_t e = hipEventRecord(ev[0], stream);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((row_stats_kernel<DT, VEC, CHECK>), dim3((unsigned)grid1), dim3(kThreads),
+                     0, stream, a->target_logits, a->draft_logits, R_t, rows, a->ld,
+                     ctx->vocab, ctx->tasks_per_row, ec, partials, counters, a->num_seqs,
+                     a->status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev) {
+    e = hipEventRecord(ev[1], stream);
+    if (e != hipSuccess) return e;
+  }
+
+  // kernel 2: G workgroups per sequence, enough to cover the chip
+  const int64_t target_wgs = (int64_t)ctx->cu_count * 4;
+  int64_t G = ceil_div(target_wgs, B);
+  if (G > ctx->num_tiles) G = ctx->num_tiles;
+  if (G < 1) G = 1;
+  if (ev) {
+    e = hipEventRecord(ev[2], stream);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((accept_draw_kernel<DT, VEC, CHECK>), dim3((unsigned)(B * G)),
+                     dim3(kThreads), 0, stream, a->target_logits, a->draft_logits, a->ld,
+                     ctx->vocab, R_t, R_d, a->cu_draft, a->draft_tokens, a->uniforms, ec,
+                     partials, ctx->tasks_per_row, tiles, counters, ctx->num_tiles, (int)G,
+                     a->out_tokens, a->out_num_accepted, a->out_p_draft, a->out_q_draft,
+                     a->out_residual_sum, a->status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev) {
+    e = hipEventRecord(ev[3], stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int DT>
+hipError_t dispatch_vec(const spec_verify_ctx* ctx, const spec_verify_args* a,
+                        hipStream_t s, bool vec, bool check) {
+  if (vec) return check ? launch_all<DT, true, true>(ctx, a, s) : launch_all<DT, true, false>(ctx, a, s);
+  return check ? launch_all<DT, false, true>(ctx, a, s) : launch_all<DT, false, false>(ctx, a, s);
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_create(spec_verify_ctx** out, int device, int64_t vocab, int dtype,
+                       int32_t max_seqs, int64_t max_draft_rows, uint32_t flags,
+                       size_t* workspace_bytes) {
+  if (!out) return SPEC_VERIFY_EINVAL;
+  *out = nullptr;
+  if (dtype != SPEC_VERIFY_F32 && dtype != SPEC_VERIFY_BF16) return SPEC_VERIFY_EUNSUPPORTED;
+  if (vocab <= 0 || vocab > INT32_MAX) return SPEC_VERIFY_EUNSUPPORTED;
+  if (max_seqs < 0 || max_draft_rows < 0 || device < 0) return SPEC_VERIFY_EINVAL;
+  if ((flags & ~SPEC_VERIFY_FLAG_CHECK) != 0) return SPEC_VERIFY_EINVAL;
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess) return hip_fail(e);
+  if (device >= count) return SPEC_VERIFY_EINVAL;
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_fail(e);
+  spec_verify_ctx* c = new (std::nothrow) spec_verify_ctx();
+  if (!c) return SPEC_VERIFY_EINVAL;
+  c->device = device;
+  c->vocab = vocab;
+  c->dtype = dtype;
+  c->max_seqs = max_seqs;
+  c->max_draft_rows = max_draft_rows;
+  c->flags = flags;
+  c->cu_count = cus > 0 ? cus : 1;
+  c->tasks_per_row = ceil_div(vocab, sv::kWaveTaskElems);
+  c->num_tiles = ceil_div(vocab, sv::kTileElems);
+  c->layout = make_layout(max_seqs, max_draft_rows, c->tasks_per_row, c->num_tiles);
+  if (workspace_bytes) *workspace_bytes = c->layout.total;
+  *out = c;
+  return SPEC_VERIFY_OK;
+}
+
+int spec_verify_query_workspace(int64_t vocab, int32_t max_seqs, int64_t max_draft_rows,
+                                size_t* workspace_bytes) {
+  if (!workspace_bytes || max_seqs < 0 || max_draft_rows < 0) return SPEC_VERIFY_EINVAL;
+  if (vocab <= 0 || vocab > INT32_MAX) return SPEC_VERIFY_EUNSUPPORTED;
+  *workspace_bytes = make_layout(max_seqs, max_draft_rows, ceil_div(vocab, sv::kWaveTaskElems),
+                                 ceil_div(vocab, sv::kTileElems))
+                         .total;
+  return SPEC_VERIFY_OK;
+}
+
+size_t spec_verify_workspace_size(const spec_verify_ctx* ctx) {
+  return ctx ? ctx->layout.total : 0;
+}
+
+int spec_verify_num_kernels(const spec_verify_ctx* ctx) { return ctx ? 2 : 0; }
+
+int spec_verify_run(const spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_stream) {
+  if (!ctx || !a) return SPEC_VERIFY_EINVAL;
+  const int64_t B = a->num_seqs;
+  const int64_t R_d = a->total_draft_rows;
+  if (B < 0 || R_d < 0) return SPEC_VERIFY_EINVAL;
+  if (!(a->temperature > 0.0f) || !std::isfinite(a->temperature)) return SPEC_VERIFY_EINVAL;
+  if (a->ld < ctx->vocab) return SPEC_VERIFY_EINVAL;
+  if (B > ctx->max_seqs || R_d > ctx->max_draft_rows) return SPEC_VERIFY_ECAPACITY;
+  if (B == 0) return SPEC_VERIFY_OK;
+  const size_t esize = ctx->dtype == SPEC_VERIFY_BF16 ? 2 : 4;
+  if (!a->cu_draft || !a->target_logits || !a->uniforms || !a->out_tokens ||
+      !a->out_num_accepted || !a->workspace)
+    return SPEC_VERIFY_EINVAL;
+  if (R_d > 0 && (!a->draft_logits || !a->draft_tokens)) return SPEC_VERIFY_EINVAL;
+  if (!aligned(a->target_logits, esize) || (a->draft_logits && !aligned(a->draft_logits, esize)) ||
+      !aligned(a->cu_draft, 4) || !aligned(a->uniforms, 4) || !aligned(a->out_tokens, 4) ||
+      !aligned(a->out_num_accepted, 4) || !aligned(a->workspace, kAlign))
+    return SPEC_VERIFY_EINVAL;
+  if (a->workspace_bytes < ctx->layout.total) return SPEC_VERIFY_ECAPACITY;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e);
+  if (cur != ctx->device) return SPEC_VERIFY_EINVAL;
+
+  const bool vec = aligned(a->target_logits, 16) &&
+                   (R_d == 0 || aligned(a->draft_logits, 16)) &&
+                   ((size_t)a->ld * esize) % 16 == 0;
+  const bool check = (ctx->flags & SPEC_VERIFY_FLAG_CHECK) != 0;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  e = ctx->dtype == SPEC_VERIFY_BF16 ? dispatch_vec<1>(ctx, a, s, vec, check)
+                                     : dispatch_vec<0>(ctx, a, s, vec, check);
+  if (e != hipSuccess) return hip_fail(e);
+  return SPEC_VERIFY_OK;
+}
+
+int spec_verify_destroy(spec_verify_ctx* ctx) {
+  delete ctx;
+  return SPEC_VERIFY_OK;
+}
+
+const char* spec_verify_status_string(int status) {
+  switch (status) {
+    case SPEC_VERIFY_OK: return "ok";
+    case SPEC_VERIFY_EINVAL: return "invalid argument";
+    case SPEC_VERIFY_EUNSUPPORTED: return "unsupported dtype or vocabulary size";
+    case SPEC_VERIFY_ECAPACITY: return "capacity exceeded (batch, draft rows or workspace)";
+    case SPEC_VERIFY_EHIP: return "HIP runtime error (see spec_verify_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int spec_verify_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

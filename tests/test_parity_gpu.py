@@ -1,0 +1,185 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Every case prints its name before touching the GPU.  Sizes: the five named
+workloads at full size (the launch configuration the benchmark times), plus
+reduced and edge-case batches that span several tiles and ragged tails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.gpu_helpers import compare, log, make_verifier, run_gpu, to_device
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _check(inp, label, **kw):
+    log(f"[case] {label}: B={inp.num_seqs} R_t={inp.target_rows} V={inp.vocab} "
+        f"{inp.dtype} T={inp.temperature}")
+    ora = oracle.verify_inputs(inp)
+    gpu = run_gpu(inp, **kw)
+    rep = compare(inp, gpu, ora, label=label)
+    assert gpu.status == 0, f"{label}: status {gpu.status:#x}"
+    return rep
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_named_workload_full_size(idx):
+    inp = W.config(idx)
+    rep = _check(inp, f"workload {idx} ({inp.name})")
+    assert rep.flagged <= max(3, inp.num_seqs // 10)
+
+
+@pytest.mark.parametrize("seed", [101, 102, 103])
+def test_named_workload_other_seeds_reduced(seed):
+    for idx in (2, 3, 4, 5):
+        inp = W.config(idx, seed=seed, num_seqs=16)
+        _check(inp, f"workload {idx} seed {seed} B=16")
+
+
+@pytest.mark.parametrize("V", [1, 5, 8, 63, 1000, 4097, 32000, 128256, 152064])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_vocab_sizes(V, dtype):
+    T = {1: 1.3, 5: 0.7, 8: 1.0, 63: 0.8}.get(V, 1.0)
+    gam = [0, 1, 4, 8, 3]
+    inp = W.build(f"V{V}", 7000 + V, gam, V, dtype, T, W.boosted_top_rows(2.0, 5, 4.0), 1.0)
+    _check(inp, f"V={V} {dtype}")
+
+
+@pytest.mark.parametrize("T", [0.7, 0.8, 1.0, 1.3])
+def test_temperatures(T):
+    inp = W.build(f"T{T}", 55, [2, 6, 0, 8, 5, 1], 32000, W.BF16, T,
+                  W.boosted_random_ids_rows(3.0, 20, 8.0), 1.0)
+    _check(inp, f"T={T}")
+
+
+def test_ragged_batch_with_long_drafts():
+    """gamma up to 70 (more than one 64-lane ballot window) mixed with 0."""
+    gam = [70, 0, 3, 65, 64, 0, 1, 63]
+    inp = W.build("long", 91, gam, 2000, W.BF16, 1.0, W.iid_normal_rows(1.0), 0.05)
+    _check(inp, "gamma up to 70")
+    inp2 = W.build("long-identical", 92, gam, 3000, W.BF16, 1.0, W.iid_normal_rows(2.0),
+                   0.0, draft_copy=lambda b: True)
+    ora = oracle.verify_inputs(inp2)
+    assert (ora.num_accepted == inp2.gammas).all()
+    _check(inp2, "gamma up to 70, draft == target")
+
+
+def test_identical_rows_always_accepted():
+    inp = W.build("ident", 3, [4] * 64, 128256, W.BF16, 1.0,
+                  W.boosted_top_rows(2.0, 50, 6.0), 0.0, draft_copy=lambda b: True)
+    inp.uniforms[::2] = np.float32(1 - 2 ** -24)
+    gpu = run_gpu(inp)
+    np.testing.assert_array_equal(gpu.num_accepted, inp.gammas)
+    _check(inp, "draft == target, u near 1")
+
+
+def test_extreme_uniforms():
+    inp = W.config(2, seed=8, num_seqs=32)
+    u = inp.uniforms
+    u[0::3] = np.float32(0.0)
+    u[1::3] = np.float32(1 - 2 ** -24)
+    _check(inp, "u in {0, 1-2^-24}")
+
+
+def test_minus_inf_logits():
+    inp = W.build("neginf", 17, [3, 0, 5, 2], 5000, W.BF16, 0.8, W.iid_normal_rows(2.0), 0.7)
+    rng = np.random.default_rng(1)
+    neg = np.uint16(0xFF80)
+    for arr in (inp.target_logits, inp.draft_logits):
+        mask = rng.random(arr.shape) < 0.3
+        arr[mask] = neg
+    # keep the drafted tokens finite under q (draft tokens are samples of q)
+    for r, x in enumerate(inp.draft_tokens):
+        if inp.draft_logits[r, x] == neg:
+            inp.draft_logits[r, x] = np.uint16(0x3F80)   # 1.0
+    # whole tiles of -inf in some rows
+    inp.target_logits[1, :2048 * 2] = neg
+    inp.target_logits[1, 3000] = np.uint16(0x4000)
+    _check(inp, "-inf logits")
+
+
+@pytest.mark.parametrize("ld_extra,offset", [(8, 0), (1, 0), (0, 1), (3, 5)])
+def test_row_pitch_and_alignment(ld_extra, offset):
+    """Padded pitch (vector path with a ragged last group), odd pitch and a
+    misaligned base (element-wise path): identical results."""
+    inp = W.build("pitch", 12, [2, 5, 0, 3], 4003, W.BF16, 1.0,
+                  W.boosted_top_rows(2.0, 20, 5.0), 1.0)
+    ora = oracle.verify_inputs(inp)
+    gpu = run_gpu(inp, ld=inp.vocab + ld_extra, offset=offset)
+    compare(inp, gpu, ora, label=f"ld=V+{ld_extra} offset={offset}")
+    base = run_gpu(inp)
+    np.testing.assert_array_equal(gpu.out_tokens, base.out_tokens)
+    np.testing.assert_array_equal(gpu.num_accepted, base.num_accepted)
+
+
+def test_empty_batch_is_a_noop():
+    from rejection_sampling_verify_08_amd import SpecVerifier
+    sv = SpecVerifier(100, "bf16", max_seqs=4, max_draft_rows=8)
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t = torch.zeros(0, 100, dtype=torch.bfloat16, device="cuda")
+    tok = torch.zeros(0, dtype=torch.int32, device="cuda")
+    u = torch.zeros(0, dtype=torch.float32, device="cuda")
+    out = sv(cu, t, t, tok, u, 1.0)
+    torch.cuda.synchronize()
+    assert out.out_tokens.numel() == 0
+
+
+def test_argument_errors():
+    from rejection_sampling_verify_08_amd import SpecVerifier, SpecVerifyError
+    inp = W.config(1)
+    d = to_device(inp)
+    sv = make_verifier(inp)
+    with pytest.raises(SpecVerifyError, match="invalid"):
+        sv(d.cu, d.target, d.draft, d.tokens, d.uniforms, 0.0)
+    with pytest.raises(SpecVerifyError, match="invalid"):
+        sv(d.cu, d.target, d.draft, d.tokens, d.uniforms, float("nan"))
+    small = SpecVerifier(inp.vocab, "f32", max_seqs=1, max_draft_rows=2)
+    with pytest.raises(SpecVerifyError, match="capacity"):
+        small(d.cu, d.target, d.draft, d.tokens, d.uniforms, 1.0)
+    sv.workspace = sv.workspace[:16]
+    with pytest.raises(SpecVerifyError, match="capacity"):
+        sv(d.cu, d.target, d.draft, d.tokens, d.uniforms, 1.0)
+
+
+def test_device_checks_flag_bad_inputs():
+    """Bad offsets / tokens are turned into status bits by the kernels' own
+    bounds checks (the sequence is skipped, outputs -1); with the check flag,
+    bad uniforms and NaN logits are reported too."""
+    inp = W.config(2, seed=4, num_seqs=6, vocab=3000)
+    d = to_device(inp)
+    sv = make_verifier(inp, check=True)
+    d.tokens[3] = 5000                         # token >= V in sequence 0
+    d.uniforms[inp.target_row(2, 1)] = 1.5     # uniform out of range
+    d.target[inp.target_row(3, 0), 17] = float("nan")
+    out = sv(d.cu, d.target, d.draft, d.tokens, d.uniforms, inp.temperature)
+    torch.cuda.synchronize()
+    st = int(out.status.item()) & 0xFFFFFFFF
+    assert st & 2 and st & 4 and st & 8, hex(st)
+    toks = out.out_tokens.cpu().numpy()
+    assert (toks[inp.target_row(0, 0):inp.target_row(0, 5) + 1] == -1).all()
+    # broken offsets: the sequence is skipped, nothing is read out of bounds
+    cu_bad = d.cu.clone()
+    cu_bad[2] = 10 ** 6
+    out2 = sv(cu_bad, d.target, d.draft, d.tokens, d.uniforms, inp.temperature)
+    torch.cuda.synchronize()
+    assert int(out2.status.item()) & 1
+
+
+def test_deterministic_repeats():
+    inp = W.config(3, seed=9, num_seqs=32)
+    d = to_device(inp)
+    sv = make_verifier(inp)
+    first = None
+    for _ in range(20):
+        out = sv(d.cu, d.target, d.draft, d.tokens, d.uniforms, inp.temperature)
+        got = [x.cpu().numpy().copy() for x in (out.out_tokens, out.num_accepted,
+                                                 out.p_draft, out.q_draft, out.residual_sum)]
+        if first is None:
+            first = got
+        for a, b in zip(first, got):
+            assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                  b.view(np.uint32) if b.dtype == np.float32 else b)
