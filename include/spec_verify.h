@@ -55,7 +55,9 @@
  *     synchronises; inputs must stay valid until the stream passes the call.
  *   - A context is immutable after creation.  Calls on different streams
  *     may overlap if each uses its own workspace; calls that share a
- *     workspace must be ordered (same stream).
+ *     workspace must be ordered (same stream).  One call is two kernel
+ *     launches: a row-parallel statistics pass and a per-sequence finish;
+ *     the stream orders them, and no workgroup ever waits for another.
  *
  * Errors: functions return SPEC_VERIFY_OK (0) or a negative status; no C++
  * exception or abort crosses the ABI.  Argument checks happen on the host
@@ -88,7 +90,7 @@ extern "C" {
 #define SPEC_VERIFY_EINVAL -1      /* NULL required pointer, B < 0, T <= 0 or
                                       non-finite, ld < V, unaligned element
                                       pointers, wrong device, bad sizes */
-#define SPEC_VERIFY_EUNSUPPORTED -2 /* dtype not f32/bf16, V <= 0, V > 2^31-1 */
+#define SPEC_VERIFY_EUNSUPPORTED -2 /* dtype not f32/bf16, V <= 0, V > 2^21 */
 #define SPEC_VERIFY_ECAPACITY -3   /* B > max_seqs, R_d > max_draft_rows,
                                       workspace smaller than required */
 #define SPEC_VERIFY_EHIP -4        /* a HIP call failed; see
@@ -165,7 +167,8 @@ SPEC_VERIFY_API int spec_verify_create(spec_verify_ctx **out, int device,
  * first).  The workspace holds one 16-byte row-statistics partial per 4096
  * logits of every target and draft row (R_t + R_d = B + 2 R_d rows), one
  * double per 2048-logit tile of each sequence's final-draw row, and one
- * arrival counter per sequence.  Returns OK, EINVAL or EUNSUPPORTED.
+ * arrival counter per sequence (cleared inside every call).  Returns OK,
+ * EINVAL or EUNSUPPORTED.
  */
 SPEC_VERIFY_API int spec_verify_query_workspace(int64_t vocab, int32_t max_seqs,
                                                 int64_t max_draft_rows,
@@ -174,7 +177,8 @@ SPEC_VERIFY_API int spec_verify_query_workspace(int64_t vocab, int32_t max_seqs,
 /* Workspace bytes one run with this context needs (same value create gave). */
 SPEC_VERIFY_API size_t spec_verify_workspace_size(const spec_verify_ctx *ctx);
 
-/* Number of kernels one run launches (each bracketed by two timing events). */
+/* Number of kernels one run launches (each bracketed by two timing events):
+ * 2. */
 SPEC_VERIFY_API int spec_verify_num_kernels(const spec_verify_ctx *ctx);
 
 /*

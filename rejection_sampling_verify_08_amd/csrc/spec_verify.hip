@@ -30,7 +30,7 @@ int hip_fail(hipError_t e) {
 struct Layout {
   size_t partials = 0;   // Partial[(max_seqs + 2 * max_draft_rows) * tasks_per_row]
   size_t tiles = 0;      // double[max_seqs * num_tiles]
-  size_t counters = 0;   // uint32[max_seqs]
+  size_t counters = 0;   // uint32[max_seqs], cleared by the row pass of each call
   size_t total = 0;
 };
 
@@ -44,8 +44,8 @@ struct spec_verify_ctx {
   int64_t max_draft_rows;
   uint32_t flags;
   int cu_count;
-  int64_t tasks_per_row;   // wave tasks of 4096 elements per row
-  int64_t num_tiles;       // 2048-element tiles per row
+  int64_t tasks_per_row;   // wave tasks of 4096 logits per row
+  int64_t num_tiles;       // 512-logit tiles per row (tile sums live in LDS)
   Layout layout;
 };
 
@@ -86,6 +86,12 @@ sv::ExpConsts exp_consts(float temperature) {
   return c;
 }
 
+int combine_lanes(int64_t tasks_per_row) {
+  int L = 1;
+  while (L < tasks_per_row && L < 64) L <<= 1;
+  return L;
+}
+
 template <int DT, bool VEC, bool CHECK>
 hipError_t launch_all(const spec_verify_ctx* ctx, const spec_verify_args* a,
                       hipStream_t stream) {
@@ -100,46 +106,32 @@ hipError_t launch_all(const spec_verify_ctx* ctx, const spec_verify_args* a,
   double* tiles = reinterpret_cast<double*>(ws + ctx->layout.tiles);
   uint32_t* counters = reinterpret_cast<uint32_t*>(ws + ctx->layout.counters);
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(a->timing_events);
+  hipError_t e;
 
-  // kernel 1: one pass over all rows
-  const int64_t wave_tasks = rows * ctx->tasks_per_row;
-  const int64_t grid1 = ceil_div(wave_tasks, kWaves);
-  if (ev) {
-    hipError_t e = hipEventRecord(ev[0], stream);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((row_stats_kernel<DT, VEC, CHECK>), dim3((unsigned)grid1), dim3(kThreads),
-                     0, stream, a->target_logits, a->draft_logits, R_t, rows, a->ld,
-                     ctx->vocab, ctx->tasks_per_row, ec, partials, counters, a->num_seqs,
+  // kernel 1: one pass over all target and draft rows
+  const int64_t grid1 = ceil_div(rows * ctx->tasks_per_row, kStatsWaves);
+  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((row_stats_kernel<DT, VEC, CHECK>), dim3((unsigned)grid1),
+                     dim3(kStatsThreads), 0, stream, a->target_logits, a->draft_logits, R_t,
+                     rows, a->ld, ctx->vocab, ctx->tasks_per_row, ec, partials, counters, B,
                      a->status);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev) {
-    e = hipEventRecord(ev[1], stream);
-    if (e != hipSuccess) return e;
-  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
 
-  // kernel 2: G workgroups per sequence, enough to cover the chip
-  const int64_t target_wgs = (int64_t)ctx->cu_count * 4;
-  int64_t G = ceil_div(target_wgs, B);
+  // kernel 2: G workgroups per sequence, about one per compute unit in all
+  int64_t G = ctx->cu_count / B;
   if (G > ctx->num_tiles) G = ctx->num_tiles;
   if (G < 1) G = 1;
-  if (ev) {
-    e = hipEventRecord(ev[2], stream);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((accept_draw_kernel<DT, VEC, CHECK>), dim3((unsigned)(B * G)),
-                     dim3(kThreads), 0, stream, a->target_logits, a->draft_logits, a->ld,
-                     ctx->vocab, R_t, R_d, a->cu_draft, a->draft_tokens, a->uniforms, ec,
-                     partials, ctx->tasks_per_row, tiles, counters, ctx->num_tiles, (int)G,
-                     a->out_tokens, a->out_num_accepted, a->out_p_draft, a->out_q_draft,
-                     a->out_residual_sum, a->status);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev) {
-    e = hipEventRecord(ev[3], stream);
-    if (e != hipSuccess) return e;
-  }
+  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
+  const size_t lds = (size_t)ctx->num_tiles * sizeof(double);
+  hipLaunchKernelGGL((finish_kernel<DT, VEC, CHECK>), dim3((unsigned)(B * G)), dim3(kThreads),
+                     lds, stream, a->target_logits, a->draft_logits, a->ld, ctx->vocab, R_t,
+                     R_d, a->cu_draft, a->draft_tokens, a->uniforms, ec, partials,
+                     ctx->tasks_per_row, combine_lanes(ctx->tasks_per_row), ctx->num_tiles,
+                     (int)G, tiles, counters, a->out_tokens, a->out_num_accepted,
+                     a->out_p_draft, a->out_q_draft, a->out_residual_sum, a->status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
   return hipSuccess;
 }
 
@@ -162,7 +154,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int64_t vocab, int dty
   if (!out) return SPEC_VERIFY_EINVAL;
   *out = nullptr;
   if (dtype != SPEC_VERIFY_F32 && dtype != SPEC_VERIFY_BF16) return SPEC_VERIFY_EUNSUPPORTED;
-  if (vocab <= 0 || vocab > INT32_MAX) return SPEC_VERIFY_EUNSUPPORTED;
+  if (vocab <= 0 || vocab > sv::kMaxVocab) return SPEC_VERIFY_EUNSUPPORTED;
   if (max_seqs < 0 || max_draft_rows < 0 || device < 0) return SPEC_VERIFY_EINVAL;
   if ((flags & ~SPEC_VERIFY_FLAG_CHECK) != 0) return SPEC_VERIFY_EINVAL;
   int count = 0;
@@ -192,10 +184,11 @@ int spec_verify_create(spec_verify_ctx** out, int device, int64_t vocab, int dty
 int spec_verify_query_workspace(int64_t vocab, int32_t max_seqs, int64_t max_draft_rows,
                                 size_t* workspace_bytes) {
   if (!workspace_bytes || max_seqs < 0 || max_draft_rows < 0) return SPEC_VERIFY_EINVAL;
-  if (vocab <= 0 || vocab > INT32_MAX) return SPEC_VERIFY_EUNSUPPORTED;
-  *workspace_bytes = make_layout(max_seqs, max_draft_rows, ceil_div(vocab, sv::kWaveTaskElems),
-                                 ceil_div(vocab, sv::kTileElems))
-                         .total;
+  if (vocab <= 0 || vocab > sv::kMaxVocab) return SPEC_VERIFY_EUNSUPPORTED;
+  *workspace_bytes =
+      make_layout(max_seqs, max_draft_rows, ceil_div(vocab, sv::kWaveTaskElems),
+                  ceil_div(vocab, sv::kTileElems))
+          .total;
   return SPEC_VERIFY_OK;
 }
 

@@ -8,34 +8,37 @@
 //   [B] the blog.hotdry.top post on speculative decoding and dynamic
 //       batching, items 流程编排 and 硬件并行.
 //
-// Two kernels per call:
+// Two kernels per call, ordered by the stream.  Within the finishing kernel
+// the workgroups of one sequence exchange tile sums through agent-scope
+// atomic stores and loads and one arrival counter; nothing ever waits.
 //
-//   row_stats_kernel  (the HBM-bound pass, ~90% of the bytes): every target
-//     and draft row is read once.  Work is cut into wave tasks of 4096
-//     consecutive elements of one row; each lane owns 8 groups of 8
-//     consecutive elements (16-byte loads for bf16), the wave's 64 lanes
-//     cover 64 consecutive groups per load instruction.  A wave computes the
-//     exact maximum m of its raw logits and s = sum 2^(y_k), with
-//     y_k = fma(l, c_lo, fma(l, c_hi, A)), A = -m * c_hi rounded, and
-//     c_hi + c_lo = log2(e)/T.  y_k equals (l_k - m) * log2(e)/T + K up to
-//     one rounding of |y_k|, where K = (A + m c_hi) + m c_lo is a per-wave
-//     constant known exactly in double; the combine removes it.  Sums of 8
-//     terms are fp32, everything above is fp64 in a fixed order.  Each wave
-//     writes one partial {m, s}.
+//   row_stats_kernel (the HBM-bound pass, ~90% of the bytes): every target
+//     and draft row is read once ([A] 1.2 step 2: all gamma+1 positions are
+//     scored in one pass).  Work is cut into wave tasks of 4096 consecutive
+//     logits of one row; a lane owns 8 groups of 8 consecutive logits and the
+//     wave's 64 lanes cover 64 consecutive groups per 16-byte load
+//     instruction.  Loads are non-temporal (the data is consumed once).  A
+//     wave computes the exact maximum m of its raw logits and
+//       s = sum_k 2^(y_k),  y_k = fma(l_k, c_lo, fma(l_k, c_hi, A)),
+//     with A = -m * c_hi rounded to float and c_hi + c_lo = log2(e) / T.
+//     y_k = (l_k - m) log2(e)/T + K up to one rounding of |y_k|, where
+//     K = (A + m c_hi) + m c_lo is a per-task constant known exactly in
+//     double that later steps divide out.  Sums of 8 terms are fp32,
+//     everything above is fp64 in a fixed order.  Each wave task writes one
+//     partial {m, s}.
 //
-//   accept_draw_kernel  (the accept test, the stop at the first rejection,
-//     and the resample / bonus draw): G workgroups per sequence.  Each
-//     combines the sequence's row partials into exact row maxima M and
-//     normalisers s in double, evaluates r_i = p_i(x_i) / q_i(x_i) in double
-//     and finds n_b as the lowest lane of a wave ballot of !(u_i < r_i)
-//     ([A] 1.2 step 3, [D] 2.1).  It then re-reads its share of the final
-//     draw row(s) -- the rejected target/draft pair, or the bonus target row
-//     -- and writes one double per 2048-element tile of
-//     w_k = max(0, p_k - q_k) (or p_k), in a common scale.  The last
-//     workgroup of the sequence to finish (integer arrival counter; no float
-//     atomics anywhere) scans the tile sums, finds the tile holding
-//     t = u * S, re-scans that tile and writes the token.
-//
+//   finish_kernel (G 1024-thread workgroups per sequence): each combines
+//     the partials into exact row maxima M and normalisers s in double,
+//     evaluates r_i = p_i(x_i) / q_i(x_i) in double, and takes n_b as the
+//     lowest lane of a wave ballot of !(u_i < r_i) ([A] 1.2 step 3, [D] 2.1:
+//     the first rejection ends the test).  Then the G workgroups share one
+//     more read of the final-draw row(s) -- the rejected target/draft pair
+//     or the bonus target row -- computing w_k = max(0, p_k - q_k) (or p_k)
+//     in a common positive scale and one double per 2048-logit tile.  The
+//     last workgroup to arrive (an integer counter cleared by the row pass)
+//     has one wave scan the tile sums, find the tile holding t = u * S,
+//     re-scan it and write the token: the smallest k with C_k > t.
+
 // Determinism: every floating-point reduction has a fixed order; the same
 // device function produces w_k in the tile pass and in the re-scan, and the
 // code is compiled with contraction off and explicit fmaf.
@@ -46,13 +49,22 @@
 
 namespace sv {
 
-constexpr int kThreads = 256;                    // 4 wave64 per workgroup
+constexpr int kGroup = 8;                        // logits per lane group
+constexpr int kStatsThreads = 256;               // row statistics: 4 wave64
+constexpr int kStatsWaves = kStatsThreads / 64;
+constexpr int kThreads = 1024;                   // finishing: one workgroup per sequence
 constexpr int kWaves = kThreads / 64;
-constexpr int kGroup = 8;                        // elements per lane group
-constexpr int kStatsGroupsPerLane = 8;           // groups per lane per wave task
-constexpr int64_t kWaveTaskElems = 64LL * kGroup * kStatsGroupsPerLane;  // 4096
-constexpr int64_t kTileElems = (int64_t)kThreads * kGroup;              // 2048
-constexpr int kTileBatch = 64;                   // tiles per LDS flush
+constexpr int kTaskGroupsPerLane = 8;            // groups per lane per wave task
+constexpr int64_t kWaveTaskElems = 64LL * kGroup * kTaskGroupsPerLane;  // 4096
+constexpr int kTileGroupsPerLane = 4;            // a tile: one wave, 4 groups per lane
+constexpr int64_t kTileGroups = 64LL * kTileGroupsPerLane;              // 256
+constexpr int64_t kTileElems = kTileGroups * kGroup;                    // 2048
+constexpr int kTilesPerBatch = 1;                // tiles per wave per load batch
+constexpr int64_t kMaxTiles = 1024;              // LDS tile sums: V <= 2^21
+constexpr int64_t kMaxVocab = kMaxTiles * kTileElems;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct Partial {        // one wave task of one row
   float m;              // exact maximum of the raw logits (or -inf)
@@ -72,12 +84,13 @@ struct ExpConsts {
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
 
+// maximum that ignores NaN operands
 __device__ __forceinline__ float fmax_nan_ignoring(float a, float b) {
   return __builtin_fmaxf(a, b);
 }
 
 // y = fma(l, c_lo, fma(l, c_hi, A)); 2^y.  -inf logits give exactly 0
-// (c_lo > 0, and A is finite).
+// (c_lo > 0 and A is finite).
 __device__ __forceinline__ float exp_term(float l, float A, const ExpConsts& c) {
   float y = __builtin_fmaf(l, c.c_hi, A);
   y = __builtin_fmaf(l, c.c_lo, y);
@@ -128,38 +141,9 @@ __device__ __forceinline__ void status_or(uint32_t* status, uint32_t bits) {
   if (status && bits) atomicOr(status, bits);
 }
 
-// Load group `g` (elements 8g..8g+7) of a row.  Elements at or beyond V read
-// as -inf.  VEC: the row base is 16-byte aligned, full groups use 16-byte
-// loads; the ragged last group and the scalar path read element by element.
-template <int DT, bool VEC>
-__device__ __forceinline__ void load_group(const void* row, int64_t g, int64_t V,
-                                           float v[kGroup]) {
-  const int64_t e0 = g * kGroup;
-  if (DT == 1) {
-    const uint16_t* r = static_cast<const uint16_t*>(row);
-    if (VEC && e0 + kGroup <= V) {
-      uint4 q = *reinterpret_cast<const uint4*>(r + e0);
-      v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
-      v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
-      v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
-      v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j)
-        v[j] = (e0 + j < V) ? __uint_as_float((uint32_t)r[e0 + j] << 16) : -INFINITY;
-    }
-  } else {
-    const float* r = static_cast<const float*>(row);
-    if (VEC && e0 + kGroup <= V) {
-      float4 a = *reinterpret_cast<const float4*>(r + e0);
-      float4 b = *reinterpret_cast<const float4*>(r + e0 + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) v[j] = (e0 + j < V) ? r[e0 + j] : -INFINITY;
-    }
-  }
+template <int DT>
+__device__ __forceinline__ const void* row_ptr(const void* base, int64_t row, int64_t ld) {
+  return static_cast<const char*>(base) + row * ld * (DT == 1 ? 2 : 4);
 }
 
 template <int DT>
@@ -168,50 +152,53 @@ __device__ __forceinline__ float load_logit(const void* row, int64_t k) {
   return static_cast<const float*>(row)[k];
 }
 
-template <int DT>
-__device__ __forceinline__ const void* row_ptr(const void* base, int64_t row, int64_t ld) {
-  return static_cast<const char*>(base) + row * ld * (DT == 1 ? 2 : 4);
-}
-
-// ---------------------------------------------------------------- kernel 1
-
-// Raw 16-byte blocks of one wave task, kept in registers between the max pass
-// and the exponent pass.
+// One group of 8 logits as raw 16-byte blocks (bf16: one block, f32: two).
 template <int DT>
 struct GroupRaw;
 template <>
-struct GroupRaw<1> { uint4 q; };
+struct GroupRaw<1> { u32x4 q; };
 template <>
-struct GroupRaw<0> { float4 a, b; };
+struct GroupRaw<0> { f32x4 a, b; };
 
+// Full group at element e0 of a 16-byte aligned row: non-temporal 16-byte
+// loads.
+template <int DT>
+__device__ __forceinline__ void load_full_nt(const void* row, int64_t e0, GroupRaw<DT>& out) {
+  if constexpr (DT == 1) {
+    out.q = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + e0));
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + e0);
+    out.a = __builtin_nontemporal_load(p);
+    out.b = __builtin_nontemporal_load(p + 1);
+  }
+}
+
+// Group g (logits 8g..8g+7) of a row; logits at or beyond V read as -inf.
+// VEC: full groups of a 16-byte aligned row use 16-byte loads; the ragged
+// last group and unaligned rows are read element by element.
 template <int DT, bool VEC>
-__device__ __forceinline__ void load_raw(const void* row, int64_t g, int64_t V,
-                                         GroupRaw<DT>& out) {
+__device__ __forceinline__ void load_group(const void* row, int64_t g, int64_t V,
+                                           GroupRaw<DT>& out) {
   const int64_t e0 = g * kGroup;
   if (VEC && e0 + kGroup <= V) {
-    if constexpr (DT == 1) {
-      out.q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + e0);
-    } else {
-      out.a = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + e0);
-      out.b = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + e0 + 4);
-    }
-  } else {
-    float v[kGroup];
-    load_group<DT, false>(row, g, V, v);
-    if constexpr (DT == 1) {
-      // re-encode: every value came from a bf16 (or is -inf), so the top 16
-      // bits hold it exactly.
-      uint32_t h[kGroup];
+    load_full_nt<DT>(row, e0, out);
+    return;
+  }
+  if constexpr (DT == 1) {
+    const uint16_t* r = static_cast<const uint16_t*>(row);
+    uint32_t h[kGroup];
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) h[j] = __float_as_uint(v[j]) >> 16;
-      out.q.x = h[0] | (h[1] << 16);
-      out.q.y = h[2] | (h[3] << 16);
-      out.q.z = h[4] | (h[5] << 16);
-      out.q.w = h[6] | (h[7] << 16);
-    } else {
-      out.a = make_float4(v[0], v[1], v[2], v[3]);
-      out.b = make_float4(v[4], v[5], v[6], v[7]);
-    }
+    for (int j = 0; j < kGroup; ++j) h[j] = (e0 + j < V) ? (uint32_t)r[e0 + j] : 0xFF80u;
+    out.q = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                  h[6] | (h[7] << 16)};
+  } else {
+    const float* r = static_cast<const float*>(row);
+    float v[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) v[j] = (e0 + j < V) ? r[e0 + j] : -INFINITY;
+    out.a = f32x4{v[0], v[1], v[2], v[3]};
+    out.b = f32x4{v[4], v[5], v[6], v[7]};
   }
 }
 
@@ -228,55 +215,46 @@ __device__ __forceinline__ void unpack(const GroupRaw<DT>& r, float v[kGroup]) {
   }
 }
 
-// One pass over every target and draft row ([A] 1.2 step 2: the target
-// scores all gamma+1 positions; the draft rows give q).  Wave task t covers
-// row t / tasks_per_row, elements [(t % tasks_per_row) * 4096, +4096).
-template <int DT, bool VEC, bool CHECK>
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(
-    const void* __restrict__ target, const void* __restrict__ draft,
-    int64_t target_rows, int64_t total_rows, int64_t ld, int64_t V,
-    int64_t tasks_per_row, ExpConsts ec, Partial* __restrict__ partials,
-    uint32_t* __restrict__ counters, int32_t num_seqs,
-    uint32_t* __restrict__ status) {
-  // Clear the per-sequence arrival counters of the accept/draw kernel that
-  // follows on the same stream.
-  {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i < num_seqs) counters[i] = 0u;
-  }
-  const int lane = threadIdx.x & 63;
-  const int64_t task = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (task >= total_rows * tasks_per_row) return;
-  const int64_t row = task / tasks_per_row;
-  const int64_t chunk = task - row * tasks_per_row;
-  const void* rp = row < target_rows ? row_ptr<DT>(target, row, ld)
-                                     : row_ptr<DT>(draft, row - target_rows, ld);
+// ---------------------------------------------------------------- row statistics
+
+// The wave task's 8 groups (lane-strided by 64 groups) of one row.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_task(const void* rp, int64_t chunk, int64_t V, int lane,
+                                          GroupRaw<DT> raw[kTaskGroupsPerLane]) {
   const int64_t g0 = chunk * (kWaveTaskElems / kGroup);
-
-  GroupRaw<DT> raw[kStatsGroupsPerLane];
+  if (VEC && (chunk + 1) * kWaveTaskElems <= V) {
+    // the whole task is inside the row: no per-group bounds checks
 #pragma unroll
-  for (int j = 0; j < kStatsGroupsPerLane; ++j)
-    load_raw<DT, VEC>(rp, g0 + j * 64 + lane, V, raw[j]);
+    for (int j = 0; j < kTaskGroupsPerLane; ++j)
+      load_full_nt<DT>(rp, (g0 + j * 64 + lane) * kGroup, raw[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTaskGroupsPerLane; ++j)
+      load_group<DT, VEC>(rp, g0 + j * 64 + lane, V, raw[j]);
+  }
+}
 
-  // exact maximum of the raw logits (NaN inputs are ignored by fmax)
+// Exact maximum m and s = sum 2^(y_k) of one wave task (all lanes get both).
+template <int DT, bool CHECK>
+__device__ __forceinline__ void task_stats(const GroupRaw<DT> raw[kTaskGroupsPerLane],
+                                           const ExpConsts& ec, float& m_out, double& s_out,
+                                           uint32_t& bad) {
   float m = -INFINITY;
-  uint32_t bad = 0;
 #pragma unroll
-  for (int j = 0; j < kStatsGroupsPerLane; ++j) {
+  for (int j = 0; j < kTaskGroupsPerLane; ++j) {
     float v[kGroup];
     unpack<DT>(raw[j], v);
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
-      m = fmax_nan_ignoring(m, v[k]);
-      if (CHECK && !(v[k] < INFINITY) && !(v[k] == -INFINITY)) bad |= 8u;
+      m = fmax_nan_ignoring(m, v[k]);   // NaN inputs are ignored by fmax
+      if (CHECK && !(v[k] < INFINITY) && !(v[k] == -INFINITY)) bad |= SPEC_VERIFY_DEV_BAD_LOGIT;
     }
   }
   m = wave_max(m);
   const float A = shift_of(m, ec);
-
   double acc = 0.0;
 #pragma unroll
-  for (int j = 0; j < kStatsGroupsPerLane; ++j) {
+  for (int j = 0; j < kTaskGroupsPerLane; ++j) {
     float v[kGroup];
     unpack<DT>(raw[j], v);
     float e[kGroup];
@@ -285,40 +263,81 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
     const float s8 = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     acc += (double)s8;
   }
-  acc = wave_xor_sum(acc);
+  m_out = m;
+  s_out = wave_xor_sum(acc);
+}
+
+// One pass over every target and draft row ([A] 1.2 step 2: the target
+// scores all gamma+1 positions; the draft rows give q).  Wave task t covers
+// row t / tasks_per_row, logits [(t % tasks_per_row) * 4096, +4096); rows
+// [0, target_rows) are target rows, the rest draft rows.  A row's partials
+// are contiguous: partial index = row * tasks_per_row + chunk.
+template <int DT, bool VEC, bool CHECK>
+__global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(
+    const void* __restrict__ target, const void* __restrict__ draft,
+    int64_t target_rows, int64_t total_rows, int64_t ld, int64_t V,
+    int64_t tasks_per_row, ExpConsts ec, Partial* __restrict__ partials,
+    uint32_t* __restrict__ counters, int64_t num_seqs, uint32_t* __restrict__ status) {
+  // Clear the per-sequence arrival counters of the finishing kernel that
+  // follows on the same stream (the grid has more than num_seqs / 256
+  // workgroups).
+  {
+    const int64_t i = (int64_t)blockIdx.x * kStatsThreads + threadIdx.x;
+    if (i < num_seqs) counters[i] = 0u;
+  }
+  const int lane = threadIdx.x & 63;
+  const int64_t task = (int64_t)blockIdx.x * kStatsWaves + (threadIdx.x >> 6);
+  if (task >= total_rows * tasks_per_row) return;
+  const int64_t row = task / tasks_per_row;
+  const int64_t chunk = task - row * tasks_per_row;
+  const void* rp = row < target_rows ? row_ptr<DT>(target, row, ld)
+                                     : row_ptr<DT>(draft, row - target_rows, ld);
+  GroupRaw<DT> raw[kTaskGroupsPerLane];
+  load_task<DT, VEC>(rp, chunk, V, lane, raw);
+  float m;
+  double s;
+  uint32_t bad = 0;
+  task_stats<DT, CHECK>(raw, ec, m, s, bad);
   if (CHECK) bad = wave_or(bad);
   if (lane == 0) {
     Partial p;
     p.m = m;
     p.pad = 0.0f;
-    p.s = acc;
+    p.s = s;
     partials[task] = p;
     if (CHECK) status_or(status, bad);
   }
 }
 
-// ---------------------------------------------------------------- kernel 2
+// ---------------------------------------------------------------- combine
 
 struct RowNorm {
   float M;       // exact row maximum of the raw logits
   double s;      // sum_k 2^((l_k - M) log2(e)/T), in double
 };
 
-// Combine the wave partials of one row (run by one whole wave).
-__device__ __forceinline__ RowNorm combine_row(const Partial* __restrict__ part,
-                                               int64_t nparts, const ExpConsts& ec,
-                                               int lane) {
+// Combine rows r0, r0 + 1, ... of a sequence's partial table, `L` lanes per
+// row (L a power of two >= the partials per row, or 64 with a loop when a
+// row has more), so one wave combines 64 / L rows at once.
+__device__ __forceinline__ RowNorm combine_rows_packed(const Partial* __restrict__ part,
+                                                       int64_t tpr, int L, int64_t row,
+                                                       bool active, const ExpConsts& ec,
+                                                       int lane) {
+  const int sub = lane & (L - 1);
   float M = -INFINITY;
-  for (int64_t i = lane; i < nparts; i += 64) M = fmax_nan_ignoring(M, part[i].m);
-  M = wave_max(M);
+  if (active)
+    for (int64_t i = sub; i < tpr; i += L) M = fmax_nan_ignoring(M, part[row * tpr + i].m);
+  for (int o = L >> 1; o > 0; o >>= 1) M = fmax_nan_ignoring(M, __shfl_xor(M, o));
   double s = 0.0;
-  for (int64_t i = lane; i < nparts; i += 64) {
-    const Partial p = part[i];
-    if (p.m == -INFINITY) continue;
-    const double K = offset_of(p.m, shift_of(p.m, ec), ec);
-    s += p.s * exp2(((double)p.m - (double)M) * ec.c64 - K);
+  if (active) {
+    for (int64_t i = sub; i < tpr; i += L) {
+      const Partial p = part[row * tpr + i];
+      if (p.m == -INFINITY) continue;
+      const double K = offset_of(p.m, shift_of(p.m, ec), ec);
+      s += p.s * exp2(((double)p.m - (double)M) * ec.c64 - K);
+    }
   }
-  s = wave_xor_sum(s);
+  for (int o = L >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);
   RowNorm r;
   r.M = M;
   r.s = s;
@@ -334,16 +353,15 @@ struct DrawConsts {
   int residual;          // 1: residual of (p, q); 0: bonus from p
 };
 
-template <int DT, bool VEC>
-__device__ __forceinline__ void group_weights(const void* prow, const void* qrow,
-                                              int64_t g, int64_t V,
-                                              const DrawConsts& dc,
-                                              const ExpConsts& ec, float w[kGroup]) {
+template <int DT>
+__device__ __forceinline__ void weights_of(const GroupRaw<DT>& rp, const GroupRaw<DT>& rq,
+                                           const DrawConsts& dc, const ExpConsts& ec,
+                                           float w[kGroup]) {
   float lp[kGroup];
-  load_group<DT, VEC>(prow, g, V, lp);
+  unpack<DT>(rp, lp);
   if (dc.residual) {
     float lq[kGroup];
-    load_group<DT, VEC>(qrow, g, V, lq);
+    unpack<DT>(rq, lq);
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
       const float ep = exp_term(lp[k], dc.Ap, ec);
@@ -366,67 +384,42 @@ __device__ __forceinline__ float seq_sum8(const float w[kGroup]) {
 }
 
 struct SeqShared {
-  float M[2][64];        // row maxima of the current 64-row window (0 target, 1 draft)
-  double s[2][64];
-  double tile_part[kWaves][kTileBatch];
-  double wave_tot[kWaves];
-  double scan_out[3];    // total S, t = u S, exclusive prefix of the found tile
-  int64_t found_tile;
-  int64_t cand[kWaves];
-  int64_t lastpos[kWaves];
+  float M[2][64];        // row maxima of the current 64-position window
+  double s[2][64];       // (0: target rows, 1: draft rows)
   int n;                 // accepted count
-  int last;              // this workgroup finishes the sequence
-  int skip;              // the sequence is invalid and skipped
-  int final_row_valid;
-  RowNorm fp, fq;        // normalisers of the final-draw rows
+  int skip;              // nonzero: a bad draft token, the sequence is skipped
+  uint32_t bad;
 };
 
-// Combine the normalisers of target row trow0 + i (which = 0) or draft row
-// drow0 + i (which = 1) for i in [lo, hi) into sh.M/s[which][i - lo].
-__device__ __forceinline__ void combine_rows(SeqShared& sh, const Partial* partials,
-                                             int64_t tasks_per_row, int64_t row_base,
-                                             int which, int64_t lo, int64_t hi,
-                                             const ExpConsts& ec, int wave, int lane) {
-  for (int64_t i = lo + wave; i < hi; i += kWaves) {
-    const RowNorm r = combine_row(partials + (row_base + i) * tasks_per_row,
-                                  tasks_per_row, ec, lane);
-    if (lane == 0) {
-      sh.M[which][i - lo] = r.M;
-      sh.s[which][i - lo] = r.s;
-    }
-  }
-}
+// ---------------------------------------------------------------- finishing
 
+// One workgroup per sequence (blockIdx = b).  The row partials come from
+// row_stats_kernel, which ran before on the same stream: target row r owns
+// partials [r * tpr, +tpr), draft row d owns [(target_rows + d) * tpr, +tpr).
 template <int DT, bool VEC, bool CHECK>
-__global__ __launch_bounds__(kThreads) void accept_draw_kernel(
-    const void* __restrict__ target, const void* __restrict__ draft, int64_t ld,
-    int64_t V, int64_t target_rows, int64_t draft_rows,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ tokens,
-    const float* __restrict__ uniforms, ExpConsts ec,
-    const Partial* __restrict__ partials, int64_t tasks_per_row,
-    double* __restrict__ tile_sums, uint32_t* __restrict__ counters,
-    int64_t num_tiles, int wgs_per_seq, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ out_num_accepted, float* __restrict__ out_p,
-    float* __restrict__ out_q, float* __restrict__ out_residual,
+__global__ __launch_bounds__(kThreads) void finish_kernel(
+    const void* __restrict__ target, const void* __restrict__ draft, int64_t ld, int64_t V,
+    int64_t target_rows, int64_t draft_rows, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, ExpConsts ec,
+    const Partial* __restrict__ part, int64_t tpr, int combine_lanes, int64_t num_tiles,
+    int G, double* __restrict__ tile_sums, uint32_t* __restrict__ counters,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num_accepted,
+    float* __restrict__ out_p, float* __restrict__ out_q, float* __restrict__ out_residual,
     uint32_t* __restrict__ status) {
   __shared__ SeqShared sh;
+  extern __shared__ double tile_sum[];   // [num_tiles], used when G == 1
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t b = (int64_t)blockIdx.x / wgs_per_seq;
-  const int gidx = (int)((int64_t)blockIdx.x - b * wgs_per_seq);
+  const int64_t b = (int64_t)blockIdx.x / G;
+  const int g = (int)((int64_t)blockIdx.x - b * G);
 
   // ---- sequence geometry, guarded so bad offsets never index out of bounds
   const int64_t c0 = cu[b], c1 = cu[b + 1];
   const int64_t gamma = c1 - c0;
   const int64_t trow0 = c0 + b, drow0 = c0;
-  if (tid == 0) {
-    sh.skip = (c0 < 0 || gamma < 0 || c1 > draft_rows || trow0 + gamma >= target_rows) ? 1 : 0;
-    sh.n = (int)gamma;
-  }
-  __syncthreads();
-  if (sh.skip) {
-    if (gidx == 0) {
+  if (!(c0 >= 0 && gamma >= 0 && c1 <= draft_rows && trow0 + gamma < target_rows)) {
+    if (g == 0) {
       if (tid == 0) {
         out_num_accepted[b] = 0;
         if (out_residual) out_residual[b] = 0.0f;
@@ -437,121 +430,149 @@ __global__ __launch_bounds__(kThreads) void accept_draw_kernel(
     }
     return;
   }
+  const float u_final = uniforms[trow0 + gamma];   // issued early, used at the end
+  // global partial-table rows of this sequence's target row j and draft row j
+  const int64_t prow_t0 = trow0, prow_d0 = target_rows + drow0;
+  if (tid == 0) {
+    sh.bad = 0;
+    sh.n = (int)gamma;
+    sh.skip = 0;
+  }
+  __syncthreads();
 
-  // ---- accept tests in windows of 64 positions; stop at the first rejection
-  uint32_t bad = 0;
+  // ================= the last workgroup of the sequence finishes it
+
+  // ---- accept tests in windows of 64 positions; stop at the first
+  // rejection ([D] 2.1).  The window holding n also holds the normalisers
+  // of the final-draw rows (target rows run to gamma, one past the drafts).
+  const int L = combine_lanes;
+  const int rows_per_wave = 64 / L;
+  int64_t lo = 0;
   int64_t n = gamma;
-  for (int64_t lo = 0; lo < gamma; lo += 64) {
-    const int64_t hi = lo + 64 < gamma ? lo + 64 : gamma;
-    combine_rows(sh, partials, tasks_per_row, trow0, 0, lo, hi, ec, wave, lane);
-    combine_rows(sh, partials, tasks_per_row, target_rows + drow0, 1, lo, hi, ec, wave, lane);
+  for (;; lo += 64) {
+    const int64_t hi_t = lo + 64 < gamma + 1 ? lo + 64 : gamma + 1;
+    const int64_t hi_d = lo + 64 < gamma ? lo + 64 : gamma;
+    // wave 0 gathers the logits at the draft tokens first; their latency
+    // overlaps the combine below
+    int32_t x = -1;
+    float lpx = 0.0f, lqx = 0.0f, u = 0.0f;
+    const int64_t i_me = lo + lane;
+    if (wave == 0 && i_me < hi_d) {
+      x = tokens[drow0 + i_me];
+      u = uniforms[trow0 + i_me];
+      if (x >= 0 && x < V) {
+        lpx = load_logit<DT>(row_ptr<DT>(target, trow0 + i_me, ld), x);
+        lqx = load_logit<DT>(row_ptr<DT>(draft, drow0 + i_me, ld), x);
+      }
+    }
+    // combine: rows of this window, rows_per_wave at a time per wave
+    const int64_t nt = hi_t - lo, nd = hi_d - lo;
+    for (int64_t r0 = (int64_t)wave * rows_per_wave; r0 < nt + nd;
+         r0 += (int64_t)kWaves * rows_per_wave) {
+      const int64_t r = r0 + lane / L;
+      const bool active = (lane / L) < rows_per_wave && r < nt + nd;
+      const bool is_t = r < nt;
+      const int64_t j = is_t ? prow_t0 + lo + r : prow_d0 + lo + (r - nt);
+      const RowNorm rn = combine_rows_packed(part, tpr, L, j, active, ec, lane);
+      if (active && (lane & (L - 1)) == 0) {
+        const int64_t i = is_t ? r : r - nt;
+        sh.M[is_t ? 0 : 1][i] = rn.M;
+        sh.s[is_t ? 0 : 1][i] = rn.s;
+      }
+    }
     __syncthreads();
     if (wave == 0) {
-      const int64_t i = lo + lane;
-      bool reject = false;
-      if (i < hi) {
-        const int32_t x = tokens[drow0 + i];
+      bool reject = false, badtok = false;
+      uint32_t wbad = 0;
+      if (i_me < hi_d) {
         double r = 0.0;
         if (x < 0 || x >= V) {
-          bad |= SPEC_VERIFY_DEV_BAD_TOKEN;
+          badtok = true;
         } else {
-          const double lp = load_logit<DT>(row_ptr<DT>(target, trow0 + i, ld), x);
-          const double lq = load_logit<DT>(row_ptr<DT>(draft, drow0 + i, ld), x);
           const double Mp = sh.M[0][lane], Mq = sh.M[1][lane];
           const double sp = sh.s[0][lane], sq = sh.s[1][lane];
-          const double pp = exp((lp - Mp) / ec.T) / sp;   // p_i(x_i)
-          const double qq = exp((lq - Mq) / ec.T) / sq;   // q_i(x_i)
-          r = exp(((lp - Mp) - (lq - Mq)) / ec.T) * (sq / sp);
-          if (gidx == 0) {
-            if (out_p) out_p[drow0 + i] = (float)pp;
-            if (out_q) out_q[drow0 + i] = (float)qq;
-          }
+          // p_i(x) = exp((l_x - M)/T) / s with s = sum_k exp((l_k - M)/T)
+          const double pp = exp(((double)lpx - Mp) / ec.T) / sp;
+          const double qq = exp(((double)lqx - Mq) / ec.T) / sq;
+          r = exp((((double)lpx - Mp) - ((double)lqx - Mq)) / ec.T) * (sq / sp);
+          if (g == 0 && out_p) out_p[drow0 + i_me] = (float)pp;
+          if (g == 0 && out_q) out_q[drow0 + i_me] = (float)qq;
           if (CHECK) {
-            if (!(qq > 0.0)) bad |= SPEC_VERIFY_DEV_ZERO_Q;
-            if (Mp == -INFINITY || Mq == -INFINITY) bad |= SPEC_VERIFY_DEV_EMPTY_ROW;
+            if (!(qq > 0.0)) wbad |= SPEC_VERIFY_DEV_ZERO_Q;
+            if (Mp == -INFINITY || Mq == -INFINITY) wbad |= SPEC_VERIFY_DEV_EMPTY_ROW;
           }
         }
-        const float u = uniforms[trow0 + i];
-        if (CHECK && !(u >= 0.0f && u < 1.0f)) bad |= SPEC_VERIFY_DEV_BAD_UNIFORM;
+        if (CHECK && !(u >= 0.0f && u < 1.0f)) wbad |= SPEC_VERIFY_DEV_BAD_UNIFORM;
         // accept iff u < r ([A] 1.2 step 3 with the strict reading)
         reject = !((double)u < r);
       }
       const uint64_t mask = __ballot(reject);
-      const uint64_t badtok = __ballot((bad & SPEC_VERIFY_DEV_BAD_TOKEN) != 0);
+      const uint64_t btok = __ballot(badtok);
+      wbad = wave_or(wbad);
       if (lane == 0) {
-        if (badtok) sh.skip = 2;
-        else if (mask && n == gamma) sh.n = (int)(lo + __builtin_ctzll(mask));
+        sh.bad |= wbad;
+        if (btok) sh.skip = 1;
+        else if (mask) sh.n = (int)(lo + __builtin_ctzll(mask));
       }
     }
     __syncthreads();
-    if (sh.skip) break;
     n = sh.n;
-    if (n < gamma) break;          // the first rejection ends the test ([D] 2.1)
+    if (sh.skip || n < gamma || lo + 64 > gamma) break;
+    __syncthreads();   // the next window overwrites sh.M / sh.s
   }
-  if (sh.skip) {  // a draft token outside [0, V): skip the sequence
-    if (gidx == 0) {
+  if (sh.skip) {       // a draft token outside [0, V): the sequence is skipped
+    if (g == 0) {
       for (int64_t i = tid; i <= gamma; i += kThreads) out_tokens[trow0 + i] = -1;
       if (tid == 0) {
         out_num_accepted[b] = 0;
         if (out_residual) out_residual[b] = 0.0f;
+        status_or(status, sh.bad | SPEC_VERIFY_DEV_BAD_TOKEN);
       }
     }
-    bad = wave_or(bad);
-    if (gidx == 0 && tid == 0) status_or(status, bad | SPEC_VERIFY_DEV_BAD_TOKEN);
     return;
   }
-  n = sh.n;
 
   // ---- emit the accepted prefix ([B] 流程编排: keep the drafts before the
-  // first mismatch); the slot n is written by the finishing workgroup.
-  if (gidx == 0) {
+  // first mismatch); slot n is written by the draw below.
+  if (g == 0) {
     for (int64_t i = tid; i <= gamma; i += kThreads) {
       if (i < n) out_tokens[trow0 + i] = tokens[drow0 + i];
       else if (i > n) out_tokens[trow0 + i] = -1;
     }
     if (tid == 0) out_num_accepted[b] = (int32_t)n;
-    // p/q outputs of positions past the stop point were not produced above
-    // (the loop breaks at the first rejecting window); fill them here.
-    if (out_p || out_q) {
-      const int64_t done = ((n / 64) + 1) * 64;
-      for (int64_t i = done + wave; i < gamma; i += kWaves) {
-        const int32_t x = tokens[drow0 + i];
-        if (x < 0 || x >= V) continue;
-        const RowNorm rp = combine_row(partials + (trow0 + i) * tasks_per_row,
-                                       tasks_per_row, ec, lane);
-        const RowNorm rq = combine_row(partials + (target_rows + drow0 + i) * tasks_per_row,
-                                       tasks_per_row, ec, lane);
-        if (lane == 0) {
-          const double lp = load_logit<DT>(row_ptr<DT>(target, trow0 + i, ld), x);
-          const double lq = load_logit<DT>(row_ptr<DT>(draft, drow0 + i, ld), x);
-          if (out_p) out_p[drow0 + i] = (float)(exp((lp - (double)rp.M) / ec.T) / rp.s);
-          if (out_q) out_q[drow0 + i] = (float)(exp((lq - (double)rq.M) / ec.T) / rq.s);
-        }
+  }
+  // p/q at positions beyond the window that stopped the test
+  if (g == 0 && (out_p || out_q)) {
+    for (int64_t i = lo + 64 + wave; i < gamma; i += kWaves) {
+      const int32_t xi = tokens[drow0 + i];
+      if (xi < 0 || xi >= V) continue;
+      const RowNorm rp = combine_rows_packed(part, tpr, 64, prow_t0 + i, true, ec, lane);
+      const RowNorm rq = combine_rows_packed(part, tpr, 64, prow_d0 + i, true, ec, lane);
+      if (lane == 0) {
+        const double lp = load_logit<DT>(row_ptr<DT>(target, trow0 + i, ld), xi);
+        const double lq = load_logit<DT>(row_ptr<DT>(draft, drow0 + i, ld), xi);
+        if (out_p) out_p[drow0 + i] = (float)(exp((lp - (double)rp.M) / ec.T) / rp.s);
+        if (out_q) out_q[drow0 + i] = (float)(exp((lq - (double)rq.M) / ec.T) / rq.s);
       }
     }
   }
 
-  // ---- normalisers of the final-draw rows
+  // ---- final-draw weights: residual at n, or the bonus row ([A] 1.2 step 3,
+  // [D] 2.2), in the common scale s_p 2^Kp
   const int residual = n < gamma ? 1 : 0;
   const void* prow = row_ptr<DT>(target, trow0 + n, ld);
   const void* qrow = residual ? row_ptr<DT>(draft, drow0 + n, ld) : prow;
-  if (wave == 0) {
-    const RowNorm r = combine_row(partials + (trow0 + n) * tasks_per_row, tasks_per_row, ec, lane);
-    if (lane == 0) sh.fp = r;
-  } else if (wave == 1 && residual) {
-    const RowNorm r = combine_row(partials + (target_rows + drow0 + n) * tasks_per_row,
-                                  tasks_per_row, ec, lane);
-    if (lane == 0) sh.fq = r;
-  }
-  __syncthreads();
+  const float Mp = sh.M[0][n - lo];
+  const double sp = sh.s[0][n - lo];
   DrawConsts dc;
   dc.residual = residual;
-  dc.Ap = shift_of(sh.fp.M, ec);
-  const double Kp = offset_of(sh.fp.M, dc.Ap, ec);
+  dc.Ap = shift_of(Mp, ec);
+  const double Kp = offset_of(Mp, dc.Ap, ec);
   if (residual) {
-    dc.Aq = shift_of(sh.fq.M, ec);
-    const double Kq = offset_of(sh.fq.M, dc.Aq, ec);
-    const double rho = (sh.fp.s / sh.fq.s) * exp2(Kp - Kq);
+    const float Mq = sh.M[1][n - lo];
+    const double sq = sh.s[1][n - lo];
+    dc.Aq = shift_of(Mq, ec);
+    const double rho = (sp / sq) * exp2(Kp - offset_of(Mq, dc.Aq, ec));
     dc.rho_hi = (float)rho;
     dc.rho_lo = (float)(rho - (double)dc.rho_hi);
   } else {
@@ -560,163 +581,165 @@ __global__ __launch_bounds__(kThreads) void accept_draw_kernel(
     dc.rho_lo = 0.0f;
   }
 
-  // ---- tile sums of this workgroup's share of the vocabulary
-  const int64_t per = (num_tiles + wgs_per_seq - 1) / wgs_per_seq;
-  const int64_t t_lo = (int64_t)gidx * per;
+  // ---- tile sums of this workgroup's share of the tiles.  A tile is 2048
+  // logits: 256 consecutive groups, lane l holding groups l, l+64, l+128,
+  // l+192 (each 16-byte load instruction covers 1 KB of contiguous logits).
+  const int64_t per = (num_tiles + G - 1) / G;
+  const int64_t t_lo = (int64_t)g * per;
   const int64_t t_hi = t_lo + per < num_tiles ? t_lo + per : num_tiles;
-  double* ts = tile_sums + b * num_tiles;
-  for (int64_t tb = t_lo; tb < t_hi; tb += kTileBatch) {
-    const int64_t te = tb + kTileBatch < t_hi ? tb + kTileBatch : t_hi;
-    for (int64_t t = tb; t < te; ++t) {
-      float w[kGroup];
-      group_weights<DT, VEC>(prow, qrow, t * kThreads + tid, V, dc, ec, w);
-      double part = wave_xor_sum((double)seq_sum8(w));
-      if (lane == 0) sh.tile_part[wave][t - tb] = part;
-    }
-    __syncthreads();
-    for (int64_t t = tb + tid; t < te; t += kThreads) {
-      const int j = (int)(t - tb);
-      ts[t] = ((sh.tile_part[0][j] + sh.tile_part[1][j]) + sh.tile_part[2][j]) +
-              sh.tile_part[3][j];
-    }
-    __syncthreads();
-  }
-
-  // ---- arrival: the last workgroup of the sequence finishes the draw
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&counters[b], 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    sh.last = (old == (uint32_t)(wgs_per_seq - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  bad = wave_or(bad);
-  if (!sh.last) {
-    if (CHECK && gidx == 0 && tid == 0) status_or(status, bad);
-    return;
-  }
-  __threadfence();
-
-  const float u = uniforms[trow0 + gamma];
-  double S = 0.0, t_target = 0.0, P_excl = 0.0;
-  int64_t tau = -1;
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    // scan the tile sums in order (wave 0), find the tile holding t = u * S
-    if (wave == 0) {
-      double total = 0.0;
-      for (int64_t c = 0; c < num_tiles; c += 64) {
-        const double v = (c + lane < num_tiles) ? ts[c + lane] : 0.0;
-        total += __shfl(wave_incl_scan(v, lane), 63);
+  double* ts_seq = tile_sums + b * num_tiles;
+  for (int64_t t0 = t_lo + (int64_t)wave * kTilesPerBatch; t0 < t_hi;
+       t0 += (int64_t)kWaves * kTilesPerBatch) {
+    GroupRaw<DT> rp[kTilesPerBatch][kTileGroupsPerLane], rq[kTilesPerBatch][kTileGroupsPerLane];
+#pragma unroll
+    for (int v = 0; v < kTilesPerBatch; ++v)
+#pragma unroll
+      for (int j = 0; j < kTileGroupsPerLane; ++j) {
+        const int64_t gi = (t0 + v) * kTileGroups + j * 64 + lane;  // past V: all -inf
+        load_group<DT, VEC>(prow, gi, V, rp[v][j]);
+        if (residual) load_group<DT, VEC>(qrow, gi, V, rq[v][j]);
       }
-      const double t = (double)u * total;
-      double base = 0.0;
-      int64_t found = -1;
-      double found_excl = 0.0;
-      for (int64_t c = 0; c < num_tiles && found < 0; c += 64) {
-        const double v = (c + lane < num_tiles) ? ts[c + lane] : 0.0;
-        const double incl = base + wave_incl_scan(v, lane);
-        const uint64_t hit = __ballot(c + lane < num_tiles && incl > t);
-        const double prev = __shfl_up(incl, 1);
-        if (hit) {
-          const int l = __builtin_ctzll(hit);
-          found = c + l;
-          found_excl = __shfl(lane == 0 ? base : prev, l);
-        }
-        base = __shfl(incl, 63);
-      }
-      if (lane == 0) {
-        sh.found_tile = found;
-        sh.scan_out[0] = total;
-        sh.scan_out[1] = t;
-        sh.scan_out[2] = found_excl;
-      }
-    }
-    __syncthreads();
-    S = sh.scan_out[0];
-    t_target = sh.scan_out[1];
-    P_excl = sh.scan_out[2];
-    tau = sh.found_tile;
-    __syncthreads();
-    if (S > 0.0 || attempt == 1) break;
-    // Empty residual (only possible for invalid input or extreme rounding):
-    // fall back to the target row at this position, done by this workgroup.
-    bad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
-    dc.residual = 0;
-    for (int64_t tb = 0; tb < num_tiles; tb += kTileBatch) {
-      const int64_t te = tb + kTileBatch < num_tiles ? tb + kTileBatch : num_tiles;
-      for (int64_t t = tb; t < te; ++t) {
+#pragma unroll
+    for (int v = 0; v < kTilesPerBatch; ++v) {
+      float lsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kTileGroupsPerLane; ++j) {
         float w[kGroup];
-        group_weights<DT, VEC>(prow, qrow, t * kThreads + tid, V, dc, ec, w);
-        double part = wave_xor_sum((double)seq_sum8(w));
-        if (lane == 0) sh.tile_part[wave][t - tb] = part;
+        weights_of<DT>(rp[v][j], rq[v][j], dc, ec, w);
+        lsum += seq_sum8(w);
       }
-      __syncthreads();
-      for (int64_t t = tb + tid; t < te; t += kThreads) {
-        const int j = (int)(t - tb);
-        ts[t] = ((sh.tile_part[0][j] + sh.tile_part[1][j]) + sh.tile_part[2][j]) +
-                sh.tile_part[3][j];
+      const double ts = wave_xor_sum((double)lsum);
+      if (lane == 0 && t0 + v < t_hi) {
+        if (G == 1) tile_sum[t0 + v] = ts;
+        else __hip_atomic_store(&ts_seq[t0 + v], ts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      __syncthreads();
     }
   }
+  // ---- arrival: with G > 1 the tile sums cross workgroups.  They were
+  // written with agent-scope atomic stores (through to the device-coherent
+  // level); each wave waits for their acknowledgement before the barrier,
+  // then one thread counts the workgroup in.  The last of the G workgroups
+  // reads them back with agent-scope atomic loads.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (G > 1) {
+    __shared__ int last;
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(&counters[b], 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      last = (old == (uint32_t)(G - 1)) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!last) return;
+  }
+  if (wave != 0) return;
 
-  // ---- re-scan tile tau: block exclusive scan of the per-thread group sums
+  // ---- one wave finishes: scan the tile sums in order, find the tile
+  // holding t = u * S, re-scan it, take the smallest k with C_k > t.
+  auto tile_at = [&](int64_t t) -> double {
+    return G == 1 ? tile_sum[t]
+                  : __hip_atomic_load(&ts_seq[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  double total = 0.0;
+  for (int64_t c = 0; c < num_tiles; c += 64) {
+    const double v = (c + lane < num_tiles) ? tile_at(c + lane) : 0.0;
+    total += __shfl(wave_incl_scan(v, lane), 63);
+  }
+  uint32_t fbad = sh.bad;
+  DrawConsts dd = dc;
+  bool fallback = false;
+  if (!(total > 0.0)) {
+    // empty residual (invalid input or extreme rounding): draw from p_n;
+    // this wave recomputes every tile sum of the target row alone
+    fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
+    dd.residual = 0;
+    fallback = true;
+    total = 0.0;
+    for (int64_t t = 0; t < num_tiles; ++t) {
+      float lsum = 0.0f;
+      for (int j = 0; j < kTileGroupsPerLane; ++j) {
+        GroupRaw<DT> r;
+        load_group<DT, VEC>(prow, t * kTileGroups + j * 64 + lane, V, r);
+        float w[kGroup];
+        weights_of<DT>(r, r, dd, ec, w);
+        lsum += seq_sum8(w);
+      }
+      const double ts = wave_xor_sum((double)lsum);
+      if (lane == 0) tile_sum[t] = ts;   // LDS holds num_tiles doubles
+      total += ts;
+    }
+  }
+  auto tile_final = [&](int64_t t) -> double { return fallback ? tile_sum[t] : tile_at(t); };
+  const double tt = (double)u_final * total;
+  double base = 0.0, P_excl = 0.0;
+  int64_t tau = -1;
+  for (int64_t c = 0; c < num_tiles && tau < 0; c += 64) {
+    const double v = (c + lane < num_tiles) ? tile_final(c + lane) : 0.0;
+    const double incl = base + wave_incl_scan(v, lane);
+    const uint64_t hit = __ballot(c + lane < num_tiles && incl > tt);
+    const double below = __shfl_up(incl, 1);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      tau = c + l;
+      P_excl = __shfl(lane == 0 ? base : below, l);
+    }
+    base = __shfl(incl, 63);
+  }
   int64_t token = -1;
   if (tau >= 0) {
-    float w[kGroup];
-    const int64_t g = tau * kThreads + tid;
-    group_weights<DT, VEC>(prow, qrow, g, V, dc, ec, w);
-    const double incl = wave_incl_scan((double)seq_sum8(w), lane);
-    const double below = __shfl_up(incl, 1);
-    if (lane == 63) sh.wave_tot[wave] = incl;
-    __syncthreads();
-    double wbase = 0.0;
-    for (int i = 0; i < wave; ++i) wbase += sh.wave_tot[i];
-    const double excl = wbase + (lane == 0 ? 0.0 : below);
-    // first element with C_k > t inside this thread's group
-    int64_t cand = INT64_MAX;
-    float c = 0.0f;
+    // re-scan tile tau in ascending logit order: group j*64 + lane for
+    // j = 0..3, each a 64-lane scan on top of the previous groups' total
+    GroupRaw<DT> rp[kTileGroupsPerLane], rq[kTileGroupsPerLane];
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
-      c += w[k];
-      if (cand == INT64_MAX && w[k] > 0.0f && P_excl + (excl + (double)c) > t_target)
-        cand = g * kGroup + k;
+    for (int j = 0; j < kTileGroupsPerLane; ++j) {
+      const int64_t gi = tau * kTileGroups + j * 64 + lane;
+      load_group<DT, VEC>(prow, gi, V, rp[j]);
+      if (dd.residual) load_group<DT, VEC>(qrow, gi, V, rq[j]);
     }
+    double run = P_excl;
     int64_t last_pos = -1;
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k)
-      if (w[k] > 0.0f) last_pos = g * kGroup + k;
-    // block min of cand, block max of last_pos
-    for (int o = 32; o > 0; o >>= 1) {
-      const int64_t oc = __shfl_xor(cand, o);
-      const int64_t ol = __shfl_xor(last_pos, o);
-      cand = oc < cand ? oc : cand;
-      last_pos = ol > last_pos ? ol : last_pos;
-    }
-    if (lane == 0) {
-      sh.cand[wave] = cand;
-      sh.lastpos[wave] = last_pos;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int64_t best = INT64_MAX, lastp = -1;
-      for (int i = 0; i < kWaves; ++i) {
-        best = sh.cand[i] < best ? sh.cand[i] : best;
-        lastp = sh.lastpos[i] > lastp ? sh.lastpos[i] : lastp;
+    for (int j = 0; j < kTileGroupsPerLane; ++j) {
+      float w[kGroup];
+      weights_of<DT>(rp[j], rq[j], dd, ec, w);
+      const int64_t gi = tau * kTileGroups + j * 64 + lane;
+      const double incl = wave_incl_scan((double)seq_sum8(w), lane);
+      const double below = __shfl_up(incl, 1);
+      const double excl = lane == 0 ? 0.0 : below;
+      int k_hit = -1;
+      float c = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        c += w[k];
+        if (k_hit < 0 && w[k] > 0.0f && run + (excl + (double)c) > tt) k_hit = k;
+        if (w[k] > 0.0f) last_pos = gi * kGroup + k;
       }
-      token = best != INT64_MAX ? best : lastp;
+      const uint64_t hit = __ballot(k_hit >= 0);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        token = (tau * kTileGroups + j * 64 + l) * kGroup + __shfl(k_hit, l);
+        break;
+      }
+      run += __shfl(incl, 63);
+    }
+    if (token < 0) {   // rounding left t past the tile's last weight
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const int64_t ol = __shfl_xor(last_pos, o);
+        last_pos = ol > last_pos ? ol : last_pos;
+      }
+      token = last_pos;
     }
   }
-  if (tid == 0) {
+  if (lane == 0) {
     out_tokens[trow0 + n] = (int32_t)token;
     if (out_residual)
-      out_residual[b] = residual && !(bad & SPEC_VERIFY_DEV_EMPTY_RESIDUAL)
-                            ? (float)(S * exp2(-Kp) / sh.fp.s)
+      out_residual[b] = (residual && !(fbad & SPEC_VERIFY_DEV_EMPTY_RESIDUAL))
+                            ? (float)(total * exp2(-Kp) / sp)
                             : 0.0f;
-    counters[b] = 0u;
+    status_or(status, fbad);
   }
-  if (tid == 0) status_or(status, bad);
 }
 
 }  // namespace sv

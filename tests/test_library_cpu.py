@@ -78,7 +78,7 @@ def test_host_side_argument_checks_without_a_device():
     assert lib.spec_verify_create(bc(ctx), 0, 1000, 7, 1, 1, 0, bc(ws)) == binding.EUNSUPPORTED
     assert ctx.value is None
     assert lib.spec_verify_create(bc(ctx), 0, 0, 1, 1, 1, 0, bc(ws)) == binding.EUNSUPPORTED
-    assert lib.spec_verify_create(bc(ctx), 0, 1 << 31, 1, 1, 1, 0, bc(ws)) == binding.EUNSUPPORTED
+    assert lib.spec_verify_create(bc(ctx), 0, (1 << 21) + 1, 1, 1, 1, 0, bc(ws)) == binding.EUNSUPPORTED
     assert lib.spec_verify_create(bc(ctx), 0, 1000, 1, -1, 1, 0, bc(ws)) == binding.EINVAL
     assert lib.spec_verify_create(bc(ctx), 0, 1000, 1, 1, -1, 0, bc(ws)) == binding.EINVAL
     assert lib.spec_verify_create(bc(ctx), 0, 1000, 1, 1, 1, 0x80, bc(ws)) == binding.EINVAL
@@ -99,7 +99,7 @@ def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
                                      (8, 1_000_000, 3_000_000)])
 def test_workspace_covers_every_row_partial_and_tile(V, B, R_d):
     """The workspace must hold one 16-byte partial per 4096 logits of all
-    R_t + R_d = B + 2 R_d rows the statistics pass reads, plus one double per
+    R_t + R_d = B + 2 R_d rows the statistics pass reads, one double per
     2048-logit tile per sequence and one counter per sequence."""
     lib = R.load_library()
     ws = ctypes.c_size_t()
