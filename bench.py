@@ -94,6 +94,9 @@ def main() -> int:
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-kernel timing events on every n-th timed step")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run three plain device-to-device copies of this "
+                         "many MiB (a known-size reference for HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the verify step shards by sequence with "
@@ -165,6 +168,15 @@ def main() -> int:
     ms_step = (t1 - t0) * 1e3 / a.steps
     k_ms = [[ev[i][2 * k].elapsed_time(ev[i][2 * k + 1]) for i in timed] for k in range(nk)]
     k_avg = [sum(x) / len(x) for x in k_ms]
+
+    if a.copy_probe_mib > 0:
+        n = a.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     num_acc = outs[0].num_accepted.cpu().numpy()
     status = int(outs[0].status.cpu().item())
