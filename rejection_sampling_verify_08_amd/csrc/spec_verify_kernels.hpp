@@ -27,7 +27,7 @@
 //     everything above is fp64 in a fixed order.  Each wave task writes one
 //     partial {m, s}.
 //
-//   finish_kernel (G 1024-thread workgroups per sequence): each combines
+//   finish_kernel (G 512-thread workgroups per sequence): each combines
 //     the partials into exact row maxima M and normalisers s in double,
 //     evaluates r_i = p_i(x_i) / q_i(x_i) in double, and takes n_b as the
 //     lowest lane of a wave ballot of !(u_i < r_i) ([A] 1.2 step 3, [D] 2.1:
@@ -52,14 +52,13 @@ namespace sv {
 constexpr int kGroup = 8;                        // logits per lane group
 constexpr int kStatsThreads = 256;               // row statistics: 4 wave64
 constexpr int kStatsWaves = kStatsThreads / 64;
-constexpr int kThreads = 1024;                   // finishing: one workgroup per sequence
+constexpr int kThreads = 512;                    // finishing workgroup: 8 wave64
 constexpr int kWaves = kThreads / 64;
 constexpr int kTaskGroupsPerLane = 8;            // groups per lane per wave task
 constexpr int64_t kWaveTaskElems = 64LL * kGroup * kTaskGroupsPerLane;  // 4096
 constexpr int kTileGroupsPerLane = 4;            // a tile: one wave, 4 groups per lane
 constexpr int64_t kTileGroups = 64LL * kTileGroupsPerLane;              // 256
 constexpr int64_t kTileElems = kTileGroups * kGroup;                    // 2048
-constexpr int kTilesPerBatch = 1;                // tiles per wave per load batch
 constexpr int64_t kMaxTiles = 1024;              // LDS tile sums: V <= 2^21
 constexpr int64_t kMaxVocab = kMaxTiles * kTileElems;
 
@@ -325,16 +324,31 @@ __device__ __forceinline__ RowNorm combine_rows_packed(const Partial* __restrict
                                                        int lane) {
   const int sub = lane & (L - 1);
   float M = -INFINITY;
-  if (active)
-    for (int64_t i = sub; i < tpr; i += L) M = fmax_nan_ignoring(M, part[row * tpr + i].m);
-  for (int o = L >> 1; o > 0; o >>= 1) M = fmax_nan_ignoring(M, __shfl_xor(M, o));
   double s = 0.0;
-  if (active) {
-    for (int64_t i = sub; i < tpr; i += L) {
-      const Partial p = part[row * tpr + i];
-      if (p.m == -INFINITY) continue;
+  if (tpr <= L) {
+    // one partial per lane: a single load feeds both reductions
+    const bool have = active && sub < tpr;
+    Partial p;
+    p.m = -INFINITY;
+    p.s = 0.0;
+    if (have) p = part[row * tpr + sub];
+    M = p.m;
+    for (int o = L >> 1; o > 0; o >>= 1) M = fmax_nan_ignoring(M, __shfl_xor(M, o));
+    if (have && p.m != -INFINITY) {
       const double K = offset_of(p.m, shift_of(p.m, ec), ec);
-      s += p.s * exp2(((double)p.m - (double)M) * ec.c64 - K);
+      s = p.s * exp2(((double)p.m - (double)M) * ec.c64 - K);
+    }
+  } else {
+    if (active)
+      for (int64_t i = sub; i < tpr; i += L) M = fmax_nan_ignoring(M, part[row * tpr + i].m);
+    for (int o = L >> 1; o > 0; o >>= 1) M = fmax_nan_ignoring(M, __shfl_xor(M, o));
+    if (active) {
+      for (int64_t i = sub; i < tpr; i += L) {
+        const Partial p = part[row * tpr + i];
+        if (p.m == -INFINITY) continue;
+        const double K = offset_of(p.m, shift_of(p.m, ec), ec);
+        s += p.s * exp2(((double)p.m - (double)M) * ec.c64 - K);
+      }
     }
   }
   for (int o = L >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);
@@ -588,30 +602,26 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
   const int64_t t_lo = (int64_t)g * per;
   const int64_t t_hi = t_lo + per < num_tiles ? t_lo + per : num_tiles;
   double* ts_seq = tile_sums + b * num_tiles;
-  for (int64_t t0 = t_lo + (int64_t)wave * kTilesPerBatch; t0 < t_hi;
-       t0 += (int64_t)kWaves * kTilesPerBatch) {
-    GroupRaw<DT> rp[kTilesPerBatch][kTileGroupsPerLane], rq[kTilesPerBatch][kTileGroupsPerLane];
-#pragma unroll
-    for (int v = 0; v < kTilesPerBatch; ++v)
+  {
+    for (int64_t t = t_lo + wave; t < t_hi; t += kWaves) {
+      GroupRaw<DT> cp[kTileGroupsPerLane], cq[kTileGroupsPerLane];
 #pragma unroll
       for (int j = 0; j < kTileGroupsPerLane; ++j) {
-        const int64_t gi = (t0 + v) * kTileGroups + j * 64 + lane;  // past V: all -inf
-        load_group<DT, VEC>(prow, gi, V, rp[v][j]);
-        if (residual) load_group<DT, VEC>(qrow, gi, V, rq[v][j]);
+        const int64_t gi = t * kTileGroups + j * 64 + lane;   // past V: all -inf
+        load_group<DT, VEC>(prow, gi, V, cp[j]);
+        if (residual) load_group<DT, VEC>(qrow, gi, V, cq[j]);
       }
-#pragma unroll
-    for (int v = 0; v < kTilesPerBatch; ++v) {
       float lsum = 0.0f;
 #pragma unroll
       for (int j = 0; j < kTileGroupsPerLane; ++j) {
         float w[kGroup];
-        weights_of<DT>(rp[v][j], rq[v][j], dc, ec, w);
+        weights_of<DT>(cp[j], cq[j], dc, ec, w);
         lsum += seq_sum8(w);
       }
       const double ts = wave_xor_sum((double)lsum);
-      if (lane == 0 && t0 + v < t_hi) {
-        if (G == 1) tile_sum[t0 + v] = ts;
-        else __hip_atomic_store(&ts_seq[t0 + v], ts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) {
+        if (G == 1) tile_sum[t] = ts;
+        else __hip_atomic_store(&ts_seq[t], ts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -697,6 +707,16 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
       load_group<DT, VEC>(prow, gi, V, rp[j]);
       if (dd.residual) load_group<DT, VEC>(qrow, gi, V, rq[j]);
     }
+    // the four 64-lane scans are independent; their totals chain in order.
+    // The weights are recomputed for the search (same code, same values)
+    // rather than held, to keep register pressure down.
+    double incl[kTileGroupsPerLane];
+#pragma unroll
+    for (int j = 0; j < kTileGroupsPerLane; ++j) {
+      float w[kGroup];
+      weights_of<DT>(rp[j], rq[j], dd, ec, w);
+      incl[j] = wave_incl_scan((double)seq_sum8(w), lane);
+    }
     double run = P_excl;
     int64_t last_pos = -1;
 #pragma unroll
@@ -704,8 +724,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
       float w[kGroup];
       weights_of<DT>(rp[j], rq[j], dd, ec, w);
       const int64_t gi = tau * kTileGroups + j * 64 + lane;
-      const double incl = wave_incl_scan((double)seq_sum8(w), lane);
-      const double below = __shfl_up(incl, 1);
+      const double below = __shfl_up(incl[j], 1);
       const double excl = lane == 0 ? 0.0 : below;
       int k_hit = -1;
       float c = 0.0f;
@@ -716,12 +735,11 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
         if (w[k] > 0.0f) last_pos = gi * kGroup + k;
       }
       const uint64_t hit = __ballot(k_hit >= 0);
-      if (hit) {
+      if (token < 0 && hit) {
         const int l = __builtin_ctzll(hit);
         token = (tau * kTileGroups + j * 64 + l) * kGroup + __shfl(k_hit, l);
-        break;
       }
-      run += __shfl(incl, 63);
+      run += __shfl(incl[j], 63);
     }
     if (token < 0) {   // rounding left t past the tile's last weight
 #pragma unroll

@@ -183,3 +183,48 @@ def test_deterministic_repeats():
         for a, b in zip(first, got):
             assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                                   b.view(np.uint32) if b.dtype == np.float32 else b)
+
+
+def test_lossless_on_gpu_one_launch():
+    """Losslessness measured on the GPU path itself: 10^6 sequences in one
+    launch, V = 8, gamma = 3, every sequence with the same target/draft rows,
+    draft tokens drawn from q, fresh uniforms.  Among sequences reaching
+    position i, the emitted token follows p_i (chi-square, Bonferroni over
+    positions); the pass rate at i is sum_k min(p_i, q_i).  The outputs must
+    also equal the oracle's bit for bit outside flagged ties."""
+    from scipy import special, stats
+    rng = np.random.default_rng(606)
+    V, g, N = 8, 3, 1_000_000
+    tgt_rows = (rng.standard_normal((g + 1, V)) * 1.2).astype(np.float32)
+    dft_rows = (tgt_rows[:g] + rng.standard_normal((g, V)) * 1.0).astype(np.float32)
+    p = [special.softmax(tgt_rows[i].astype(np.float64)) for i in range(g + 1)]
+    q = [special.softmax(dft_rows[i].astype(np.float64)) for i in range(g)]
+    tokens = np.stack([rng.choice(V, size=N, p=q[i]) for i in range(g)], axis=1)
+    inp = W.VerifyInputs(
+        name="lossless", vocab=V, dtype=W.F32, temperature=1.0,
+        gammas=np.full(N, g, np.int32), cu_draft=W.cu_from_gammas([g] * N),
+        target_logits=np.tile(tgt_rows, (N, 1)), draft_logits=np.tile(dft_rows, (N, 1)),
+        draft_tokens=tokens.reshape(-1).astype(np.int32),
+        uniforms=W.uniform_grid24(rng, N * (g + 1)))
+    log(f"[case] lossless one launch: B={N} V={V} gamma={g}")
+    gpu = run_gpu(inp)
+    out = gpu.out_tokens.reshape(N, g + 1)
+    n = gpu.num_accepted
+    alpha_level = 1e-3 / (2 * g + 1)
+    for i in range(g + 1):
+        mask = n >= i
+        counts = np.bincount(out[mask, i], minlength=V)
+        assert counts.sum() == mask.sum()
+        assert stats.chisquare(counts, mask.sum() * p[i]).pvalue > alpha_level, (i, counts)
+        if i < g:
+            a = np.minimum(p[i], q[i]).sum()
+            reached, passed = mask.sum(), (n >= i + 1).sum()
+            z = (passed - reached * a) / np.sqrt(reached * a * (1 - a))
+            assert abs(z) < stats.norm.isf(alpha_level / 2), (i, z)
+    ora = oracle.verify_inputs(inp)
+    flagged = ora.flagged != 0
+    same = (gpu.num_accepted == ora.num_accepted) & \
+        (out == ora.out_tokens.reshape(N, g + 1)).all(axis=1)
+    log(f"[parity] lossless one launch: seqs={N} flagged={int(flagged.sum())} "
+        f"differing={int((~same).sum())}")
+    assert (same | flagged).all()
