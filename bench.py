@@ -12,6 +12,12 @@ Prints one JSON line: verified rows/s (value), whole-step HBM GB/s, the
 roofline of the dominant kernel (the row-statistics pass, HBM-bound; its
 duration from HIP events recorded on the launch stream around each kernel),
 and the float64 CPU oracle timed on this host as a reported baseline.
+
+The same line carries, under "modes", the same measurement for the two other
+entry points on the same batch with deterministic drafts (each draft token
+the first maximum of its draft row): greedy verification
+(spec_verify_run_greedy) and point-mass-draft verification
+(spec_verify_run_point_drafts).
 """
 from __future__ import annotations
 
@@ -29,7 +35,7 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "verified rows/s + achieved HBM GB/s (% peak), B=128 γ=8 V=128256 bf16"
 PMC_FILE = os.path.join(ROOT, "profiles", "row_stats_kernel_B128_g8_V128256_bf16.pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_08_amd", "csrc", f)
-                  for f in ("spec_verify_kernels.hpp", "spec_verify.hip")]
+                  for f in ("spec_verify_kernels.hpp", "greedy_kernels.hpp", "spec_verify.hip")]
 
 
 def kernel_source_hash() -> str:
@@ -51,19 +57,27 @@ def traffic_from_profile(src_hash: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def algorithmic_bytes(inp, num_accepted):
-    """Minimum bytes one step must move: every logit row once, plus the
-    final-draw row(s) once more (2 rows after a rejection, 1 for the bonus),
-    plus tokens, uniforms, offsets and outputs."""
-    import numpy as np
+def algorithmic_bytes(inp, num_accepted, mode="sampled"):
+    """Minimum bytes one step must move.
+
+    sampled: every target and draft row once, the final-draw row(s) once more
+      (2 rows after a rejection, 1 for the bonus), tokens, uniforms, offsets,
+      outputs (tokens, counts, p/q at the drafts, residual sums).
+    point:   every target row once, one final-draw target row per sequence
+      once more, tokens, uniforms, offsets, the same outputs.
+    greedy:  every target row once, tokens, offsets, tokens and counts out.
+    Returns (first-pass logit bytes, re-read logit bytes, other bytes)."""
     e = 2 if inp.dtype == "bf16" else 4
     V = inp.vocab
-    first = (inp.target_rows + inp.draft_rows) * V * e
+    B, R_t, R_d = inp.num_seqs, inp.target_rows, inp.draft_rows
+    io = R_d * 4 + (B + 1) * 4 + R_t * 4 + B * 4          # tokens, cu, out tokens, counts
+    if mode == "greedy":
+        return R_t * V * e, 0, io
+    io += R_t * 4 + R_d * 8 + B * 4                        # uniforms, p/q, residual sums
+    if mode == "point":
+        return R_t * V * e, B * V * e, io
     rejected = int((num_accepted < inp.gammas).sum())
-    reread = (2 * rejected + (inp.num_seqs - rejected)) * V * e
-    small = (inp.draft_rows * 4 + inp.target_rows * 4 + (inp.num_seqs + 1) * 4 +
-             inp.target_rows * 4 + inp.num_seqs * 4 + inp.draft_rows * 8 + inp.num_seqs * 4)
-    return first, reread, small
+    return (R_t + R_d) * V * e, (2 * rejected + (B - rejected)) * V * e, io
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -94,6 +108,8 @@ def main() -> int:
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-kernel timing events on every n-th timed step")
+    ap.add_argument("--skip-modes", action="store_true",
+                    help="time only spec_verify_run (not the greedy and point-draft entry points)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run three plain device-to-device copies of this "
                          "many MiB (a known-size reference for HBM byte counters)")
@@ -148,26 +164,32 @@ def main() -> int:
             e.record(stream)          # creates the underlying hipEvent
         return evs
 
-    for i in range(a.warmup):
-        t, d = sets[i % len(sets)]
-        sv(cu, t, d, tok, uni, inp.temperature, out=outs[i % len(sets)], stream=stream)
-    # Kernel durations come from HIP events recorded on the launch stream
-    # around each kernel of every `event_every`-th timed step; a timing event
-    # costs several microseconds of stream time, so recording them on every
-    # step would inflate the step time the headline divides by.
-    timed = list(range(0, a.steps, a.event_every))
-    ev = {i: make_events(2 * nk) for i in timed}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(a.steps):
+    def timed(call):
+        """Warm up, then time a.steps calls; per-kernel HIP events on every
+        `event_every`-th step (a timing event costs several microseconds of
+        stream time, so recording them on every step would inflate the step
+        time the headline divides by)."""
+        for i in range(a.warmup):
+            call(i, None)
+        steps_ev = list(range(0, a.steps, a.event_every))
+        ev = {i: make_events(2 * nk) for i in steps_ev}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            call(i, ev.get(i))
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms = (t1 - t0) * 1e3 / a.steps
+        k_ms = [[ev[i][2 * k].elapsed_time(ev[i][2 * k + 1]) for i in steps_ev]
+                for k in range(nk)]
+        return ms, [sum(x) / len(x) for x in k_ms]
+
+    def sampled_step(i, events):
         t, d = sets[i % len(sets)]
         sv(cu, t, d, tok, uni, inp.temperature, out=outs[i % len(sets)], stream=stream,
-           timing_events=ev.get(i))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / a.steps
-    k_ms = [[ev[i][2 * k].elapsed_time(ev[i][2 * k + 1]) for i in timed] for k in range(nk)]
-    k_avg = [sum(x) / len(x) for x in k_ms]
+           timing_events=events)
+
+    ms_step, k_avg = timed(sampled_step)
 
     if a.copy_probe_mib > 0:
         n = a.copy_probe_mib << 20
@@ -193,6 +215,48 @@ def main() -> int:
             "traffic": traffic, "kernel": "row_stats_kernel",
             "kernel_avg_us": round(k_avg[0] * 1e3, 2),
             "algorithmic_bytes_per_launch": first}
+
+    # the other two entry points on the same target rows, deterministic drafts
+    modes = {}
+    if not a.skip_modes:
+        det = W.with_deterministic_drafts(inp)
+        tok_det = torch.from_numpy(det.draft_tokens).to(dev)
+
+        def greedy_step(i, events):
+            t, _ = sets[i % len(sets)]
+            sv.greedy(cu, t, tok_det, out=outs[i % len(sets)], stream=stream,
+                      timing_events=events)
+
+        def point_step(i, events):
+            t, _ = sets[i % len(sets)]
+            sv.point_drafts(cu, t, tok_det, uni, inp.temperature, out=outs[i % len(sets)],
+                            stream=stream, timing_events=events)
+
+        for name, step, kname in (("greedy", greedy_step, "argmax_kernel"),
+                                  ("point_drafts", point_step, "row_stats_kernel")):
+            m_ms, m_k = timed(step)
+            m_acc = outs[0].num_accepted.cpu().numpy()
+            m_first, m_reread, m_small = algorithmic_bytes(
+                det, m_acc, "greedy" if name == "greedy" else "point")
+            m_bytes = m_first + m_reread + m_small
+            m_ach = m_first / (m_k[0] / 1e3) / 1e9
+            modes[name] = {
+                "value": round(inp.target_rows / (m_ms / 1e3), 1), "unit": "verified rows/s",
+                "ms_per_step": round(m_ms, 5),
+                "hbm_gbps": round(m_bytes / (m_ms / 1e3) / 1e9, 1),
+                "step_algorithmic_bytes": m_bytes,
+                "kernel_avg_us": [round(x * 1e3, 2) for x in m_k],
+                "kernel_names": [kname, "greedy_finish_kernel" if name == "greedy"
+                                 else "finish_kernel"],
+                "mean_accepted": round(float(m_acc.mean()), 4),
+                "status": int(outs[0].status.cpu().item()),
+                "roofline": {"bound": "hbm", "achieved": round(m_ach, 1),
+                             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                             "frac": round(m_ach / PEAK_HBM_GBPS, 4), "traffic": None,
+                             "kernel": kname, "kernel_avg_us": round(m_k[0] * 1e3, 2),
+                             "algorithmic_bytes_per_launch": m_first},
+            }
+
     cpu = None
     if a.cpu_budget > 0:
         cpu = cpu_baseline(inp, a.cpu_budget)
@@ -211,6 +275,7 @@ def main() -> int:
         "kernel_names": ["row_stats_kernel", "finish_kernel"][:nk],
         "mean_accepted": round(float(num_acc.mean()), 4), "status": status,
         "roofline": roof, "cpu_baseline": cpu,
+        "modes": modes or None,
         "kernel_source_hash": src_hash,
     }
     print(json.dumps(line, ensure_ascii=False), flush=True)

@@ -178,7 +178,8 @@ SPEC_VERIFY_API int spec_verify_query_workspace(int64_t vocab, int32_t max_seqs,
 SPEC_VERIFY_API size_t spec_verify_workspace_size(const spec_verify_ctx *ctx);
 
 /* Number of kernels one run launches (each bracketed by two timing events):
- * 2. */
+ * 2, for spec_verify_run, spec_verify_run_greedy and
+ * spec_verify_run_point_drafts alike. */
 SPEC_VERIFY_API int spec_verify_num_kernels(const spec_verify_ctx *ctx);
 
 /*
@@ -192,6 +193,48 @@ SPEC_VERIFY_API int spec_verify_num_kernels(const spec_verify_ctx *ctx);
 SPEC_VERIFY_API int spec_verify_run(const spec_verify_ctx *ctx,
                                     const spec_verify_args *args,
                                     void *hip_stream);
+
+/*
+ * Greedy verification: the temperature -> 0 limit of spec_verify_run.
+ * [B] item 流程编排: the drafts are compared in order with the target's
+ * choices, the prefix before the first mismatch is kept and decoding resumes
+ * at the mismatched position.  Under greedy decoding the target's choice at
+ * a position is the argmax of its logits, and equal maxima go to the lowest
+ * token id (a reading: the page names no tie rule).  For every sequence:
+ *   n_b = the first i with draft_tokens[i] != argmax(target row i), or
+ *         gamma_b when every draft matches;
+ *   out_tokens = the drafts before n_b, then argmax(target row n_b) (the
+ *         token at the mismatch, or the bonus when n_b = gamma_b), then -1.
+ * Same argument block, layout, workspace and error behaviour as
+ * spec_verify_run.  Used: num_seqs, total_draft_rows, cu_draft,
+ * target_logits, ld, draft_tokens, out_tokens, out_num_accepted, workspace,
+ * workspace_bytes, status, timing_events.  Ignored (may be NULL / any
+ * value): draft_logits, uniforms, temperature, out_p_draft, out_q_draft,
+ * out_residual_sum.  Only the R_t target rows are read, once.  Logits must
+ * not be NaN (SPEC_VERIFY_FLAG_CHECK reports NaN and +inf as
+ * SPEC_VERIFY_DEV_BAD_LOGIT); an all -inf row has argmax 0.  Two kernels.
+ */
+SPEC_VERIFY_API int spec_verify_run_greedy(const spec_verify_ctx *ctx,
+                                           const spec_verify_args *args,
+                                           void *hip_stream);
+
+/*
+ * Verification of deterministic drafts: the draft proposes tokens without a
+ * distribution (n-gram / prompt-lookup drafting: [A] sections 1.4 and 3.3,
+ * and section 4.1 of [D]), so the draft distribution at position i is the
+ * point mass at x_i.  The rule of spec_verify_run then reads:
+ *   accept draft i iff u_i < p_i(x_i)                 (q_i(x_i) = 1);
+ *   after a rejection at j, draw from norm(max(0, p_j - delta_{x_j})), which
+ *   is p_j with x_j removed and renormalised;
+ *   when every draft passes, the bonus is drawn from p_{gamma_b}.
+ * Same argument block, uniforms, layout, workspace and error behaviour as
+ * spec_verify_run; draft_logits is ignored (may be NULL) and no draft row is
+ * read.  out_q_draft, when given, receives 1.0; out_residual_sum receives
+ * the sum of p_j over k != x_j (0 after a bonus draw).  Two kernels.
+ */
+SPEC_VERIFY_API int spec_verify_run_point_drafts(const spec_verify_ctx *ctx,
+                                                 const spec_verify_args *args,
+                                                 void *hip_stream);
 
 /* Destroy a context (NULL is accepted).  Returns OK. */
 SPEC_VERIFY_API int spec_verify_destroy(spec_verify_ctx *ctx);

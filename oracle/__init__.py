@@ -53,6 +53,13 @@ def _load():
         lib.oracle_row_softmax.restype = ctypes.c_int
         lib.oracle_row_softmax.argtypes = [P, ctypes.c_int, ctypes.c_int64,
                                            ctypes.c_float, P]
+        lib.oracle_verify_greedy.restype = ctypes.c_int
+        lib.oracle_verify_greedy.argtypes = [ctypes.c_int32, P, P, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_int, P, P, P, P]
+        lib.oracle_verify_onehot.restype = ctypes.c_int
+        lib.oracle_verify_onehot.argtypes = [
+            ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, P, P,
+            ctypes.c_float, ctypes.c_double, P, P, P, P, P, P, P]
         lib.oracle_overlap_mass.restype = ctypes.c_double
         lib.oracle_overlap_mass.argtypes = [P, P, ctypes.c_int, ctypes.c_int64,
                                             ctypes.c_float]
@@ -162,3 +169,75 @@ def overlap_mass(target_row, draft_row, temperature: float, dtype=None) -> float
     code = _dtype_code(t, dtype)
     return float(lib.oracle_overlap_mass(_ptr(t), _ptr(d), code, t.shape[0],
                                          float(temperature)))
+
+
+@dataclasses.dataclass
+class GreedyResult:
+    out_tokens: np.ndarray       # int32 [R_t]
+    num_accepted: np.ndarray     # int32 [B]
+    argmax: np.ndarray           # int32 [R_t], each target row's argmax
+
+    def emitted(self, b: int, cu: np.ndarray) -> np.ndarray:
+        t0 = int(cu[b]) + b
+        return self.out_tokens[t0:t0 + int(self.num_accepted[b]) + 1]
+
+
+def verify_greedy(num_seqs: int, cu_draft, target_logits, draft_tokens, *,
+                  vocab: int | None = None, dtype=None) -> GreedyResult:
+    """Greedy verification (argmax of each target row, lowest id on ties)."""
+    lib = _load()
+    tgt = np.ascontiguousarray(target_logits)
+    code = _dtype_code(tgt, dtype)
+    ld = tgt.shape[1]
+    V = ld if vocab is None else int(vocab)
+    cu = np.ascontiguousarray(cu_draft, dtype=np.int32)
+    tok = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    if tok.size == 0:
+        tok = np.zeros(1, dtype=np.int32)
+    B = int(num_seqs)
+    R_t = tgt.shape[0]
+    res = GreedyResult(out_tokens=np.full(R_t, -7, np.int32),
+                       num_accepted=np.zeros(B, np.int32),
+                       argmax=np.full(R_t, -7, np.int32))
+    rc = lib.oracle_verify_greedy(B, _ptr(cu), _ptr(tgt), ld, V, code, _ptr(tok),
+                                  _ptr(res.out_tokens), _ptr(res.num_accepted),
+                                  _ptr(res.argmax))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_greedy returned {rc}")
+    return res
+
+
+def verify_onehot(num_seqs: int, cu_draft, target_logits, draft_tokens, uniforms,
+                  temperature: float, *, vocab: int | None = None, dtype=None,
+                  tie_tol: float = TIE_TOL) -> OracleResult:
+    """Verification of a deterministic draft (q is the point mass at x)."""
+    lib = _load()
+    tgt = np.ascontiguousarray(target_logits)
+    code = _dtype_code(tgt, dtype)
+    ld = tgt.shape[1]
+    V = ld if vocab is None else int(vocab)
+    cu = np.ascontiguousarray(cu_draft, dtype=np.int32)
+    tok = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    if tok.size == 0:
+        tok = np.zeros(1, dtype=np.int32)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    B = int(num_seqs)
+    R_t = tgt.shape[0]
+    R_d = max(int(cu[-1]) if B > 0 else 0, 0)
+    res = OracleResult(
+        out_tokens=np.full(R_t, -7, dtype=np.int32),
+        num_accepted=np.zeros(B, dtype=np.int32),
+        p_draft=np.zeros(R_d, dtype=np.float64),
+        q_draft=np.ones(R_d, dtype=np.float64),
+        residual_sum=np.zeros(B, dtype=np.float64),
+        tie_accept=np.full(R_d, np.nan, dtype=np.float64),
+        tie_final=np.zeros(B, dtype=np.float64),
+        flagged=np.zeros(B, dtype=np.int32))
+    rc = lib.oracle_verify_onehot(
+        B, _ptr(cu), _ptr(tgt), ld, V, code, _ptr(tok), _ptr(u), float(temperature),
+        float(tie_tol), _ptr(res.out_tokens), _ptr(res.num_accepted),
+        _ptr(res.p_draft) if R_d else None, _ptr(res.residual_sum),
+        _ptr(res.tie_accept) if R_d else None, _ptr(res.tie_final), _ptr(res.flagged))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_onehot returned {rc}")
+    return res

@@ -276,3 +276,175 @@ int oracle_verify(int32_t num_seqs, const int32_t *cu_draft,
   free(Mp); free(sp); free(Mq); free(sq); free(w); free(C);
   return ORACLE_OK;
 }
+
+/*
+ * Greedy verification ([B] 流程编排: candidates are compared with the
+ * target's choice in order; at the first mismatch the matching prefix is
+ * kept and decoding restarts there).  With T -> 0 the target's choice at a
+ * position is the argmax of its logits; ties go to the lowest token id.
+ * The token emitted at the first mismatch is the target's argmax there; when
+ * every draft matches, the bonus is the argmax of the (gamma+1)-th row.
+ * out_argmax (optional, [R_t]) receives each target row's argmax.
+ */
+static int64_t row_argmax(const void *base, int dtype, int64_t row, int64_t ld,
+                          int64_t vocab) {
+  const int64_t off = row * ld;
+  int64_t best = 0;
+  double bv = load_logit(base, dtype, off);
+  for (int64_t k = 1; k < vocab; ++k) {
+    const double v = load_logit(base, dtype, off + k);
+    if (v > bv) { bv = v; best = k; }
+  }
+  return best;
+}
+
+int oracle_verify_greedy(int32_t num_seqs, const int32_t *cu_draft,
+                         const void *target_logits, int64_t ld, int64_t vocab,
+                         int dtype, const int32_t *draft_tokens,
+                         int32_t *out_tokens, int32_t *out_num_accepted,
+                         int32_t *out_argmax) {
+  if (num_seqs < 0 || vocab <= 0 || ld < vocab || (dtype != 0 && dtype != 1))
+    return ORACLE_EINVAL;
+  if (num_seqs == 0) return ORACLE_OK;
+  if (!cu_draft || !target_logits || !out_tokens || !out_num_accepted)
+    return ORACLE_EINVAL;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t gamma = (int64_t)cu_draft[b + 1] - cu_draft[b];
+    const int64_t trow0 = (int64_t)cu_draft[b] + b;
+    const int64_t drow0 = (int64_t)cu_draft[b];
+    if (gamma < 0 || (gamma > 0 && !draft_tokens)) return ORACLE_EINVAL;
+    int64_t j = gamma;
+    for (int64_t i = 0; i <= gamma; ++i) {
+      const int64_t a = row_argmax(target_logits, dtype, trow0 + i, ld, vocab);
+      if (out_argmax) out_argmax[trow0 + i] = (int32_t)a;
+    }
+    for (int64_t i = 0; i < gamma; ++i) {
+      const int64_t x = draft_tokens[drow0 + i];
+      if (x < 0 || x >= vocab) return ORACLE_EINVAL;
+      if (x != row_argmax(target_logits, dtype, trow0 + i, ld, vocab)) { j = i; break; }
+    }
+    for (int64_t i = 0; i <= gamma; ++i) {
+      int32_t v;
+      if (i < j) v = draft_tokens[drow0 + i];
+      else if (i == j) v = (int32_t)row_argmax(target_logits, dtype, trow0 + j, ld, vocab);
+      else v = -1;
+      out_tokens[trow0 + i] = v;
+    }
+    out_num_accepted[b] = (int32_t)j;
+  }
+  return ORACLE_OK;
+}
+
+/*
+ * Verification of a deterministic draft (the draft proposes tokens without a
+ * distribution, as n-gram / prompt-lookup drafting does: [A] 1.4 and 3.3,
+ * [D] 4.1).
+ * The draft distribution is then the point mass q = delta_x, so the general
+ * rule specialises to: accept x with probability min(1, p(x) / 1) = p(x), and
+ * on rejection resample from norm(max(0, p - delta_x)) = p with x removed and
+ * renormalised.  Same layout, uniforms, draw convention and diagnostics as
+ * oracle_verify; there are no draft logits.  out_q_draft is 1.
+ */
+int oracle_verify_onehot(int32_t num_seqs, const int32_t *cu_draft,
+                         const void *target_logits, int64_t ld, int64_t vocab,
+                         int dtype, const int32_t *draft_tokens,
+                         const float *uniforms, float temperature, double tie_tol,
+                         int32_t *out_tokens, int32_t *out_num_accepted,
+                         double *out_p_draft, double *out_residual_sum,
+                         double *tie_accept, double *tie_final, int32_t *flagged) {
+  if (num_seqs < 0 || vocab <= 0 || ld < vocab || (dtype != 0 && dtype != 1) ||
+      !(temperature > 0.0f) || !isfinite(temperature))
+    return ORACLE_EINVAL;
+  if (num_seqs == 0) return ORACLE_OK;
+  if (!cu_draft || !target_logits || !uniforms || !out_tokens || !out_num_accepted)
+    return ORACLE_EINVAL;
+  const double T = (double)temperature;
+  int64_t max_gamma = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t g = (int64_t)cu_draft[b + 1] - cu_draft[b];
+    if (g < 0) return ORACLE_EINVAL;
+    if (g > max_gamma) max_gamma = g;
+  }
+  if (max_gamma > 0 && !draft_tokens) return ORACLE_EINVAL;
+  double *Mp = malloc(sizeof(double) * (size_t)(max_gamma + 1));
+  double *sp = malloc(sizeof(double) * (size_t)(max_gamma + 1));
+  double *w = malloc(sizeof(double) * (size_t)vocab);
+  double *C = malloc(sizeof(double) * (size_t)vocab);
+  if (!Mp || !sp || !w || !C) { free(Mp); free(sp); free(w); free(C); return ORACLE_ENOMEM; }
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t gamma = (int64_t)cu_draft[b + 1] - cu_draft[b];
+    const int64_t trow0 = (int64_t)cu_draft[b] + b;
+    const int64_t drow0 = (int64_t)cu_draft[b];
+    int32_t flag = 0;
+    for (int64_t i = 0; i <= gamma; ++i)
+      row_normaliser(target_logits, dtype, trow0 + i, ld, vocab, T, &Mp[i], &sp[i]);
+    for (int64_t i = 0; i < gamma; ++i) {
+      const int64_t x = draft_tokens[drow0 + i];
+      if (x < 0 || x >= vocab) { free(Mp); free(sp); free(w); free(C); return ORACLE_EINVAL; }
+      if (out_p_draft) out_p_draft[drow0 + i] = prob(target_logits, dtype, trow0 + i, ld, x, T, Mp[i], sp[i]);
+      if (tie_accept) tie_accept[drow0 + i] = NAN;
+    }
+    /* accept with probability p(x): u < p(x) / q(x) with q(x) = 1 */
+    int64_t j = gamma;
+    for (int64_t i = 0; i < gamma; ++i) {
+      const int64_t x = draft_tokens[drow0 + i];
+      const double px = prob(target_logits, dtype, trow0 + i, ld, x, T, Mp[i], sp[i]) / 1.0;
+      const double u = (double)uniforms[trow0 + i];
+      const double d = fabs(u - px);
+      if (tie_accept) tie_accept[drow0 + i] = d;
+      if (d < tie_tol) flag |= 1;
+      if (!(u < px)) { j = i; break; }
+    }
+    /* residual max(0, p - delta_x): p with x removed; or the bonus row p */
+    const int64_t tj = trow0 + j;
+    for (int64_t k = 0; k < vocab; ++k) {
+      const double p = prob(target_logits, dtype, tj, ld, k, T, Mp[j], sp[j]);
+      if (j < gamma) {
+        const double q = (k == draft_tokens[drow0 + j]) ? 1.0 : 0.0;
+        w[k] = p - q > 0.0 ? p - q : 0.0;
+      } else {
+        w[k] = p;
+      }
+    }
+    double S = 0.0;
+    for (int64_t k = 0; k < vocab; ++k) { S += w[k]; C[k] = S; }
+    const double S_reported = (j < gamma) ? S : 0.0;
+    if (!(S > 0.0)) {
+      flag |= 4;
+      S = 0.0;
+      for (int64_t k = 0; k < vocab; ++k) {
+        w[k] = prob(target_logits, dtype, tj, ld, k, T, Mp[j], sp[j]);
+        S += w[k];
+        C[k] = S;
+      }
+    }
+    const double u = (double)uniforms[trow0 + gamma];
+    const double t = u * S;
+    int64_t tok = -1;
+    for (int64_t k = 0; k < vocab; ++k)
+      if (C[k] > t) { tok = k; break; }
+    if (tok < 0)
+      for (int64_t k = vocab - 1; k >= 0; --k)
+        if (w[k] > 0.0) { tok = k; break; }
+    double df = 0.0;
+    if (tok >= 0) {
+      const double lo = tok > 0 ? C[tok - 1] : 0.0;
+      df = fmin(t - lo, C[tok] - t) / S;
+      if (df < 0.0) df = 0.0;
+    }
+    if (df < tie_tol) flag |= 2;
+    for (int64_t i = 0; i <= gamma; ++i) {
+      int32_t v;
+      if (i < j) v = draft_tokens[drow0 + i];
+      else if (i == j) v = (int32_t)tok;
+      else v = -1;
+      out_tokens[trow0 + i] = v;
+    }
+    out_num_accepted[b] = (int32_t)j;
+    if (out_residual_sum) out_residual_sum[b] = S_reported;
+    if (tie_final) tie_final[b] = df;
+    if (flagged) flagged[b] = flag;
+  }
+  free(Mp); free(sp); free(w); free(C);
+  return ORACLE_OK;
+}

@@ -30,6 +30,7 @@ DEV_EMPTY_RESIDUAL = 64
 EXPORTED = ("spec_verify_create", "spec_verify_query_workspace",
             "spec_verify_workspace_size",
             "spec_verify_num_kernels", "spec_verify_run",
+            "spec_verify_run_greedy", "spec_verify_run_point_drafts",
             "spec_verify_destroy", "spec_verify_status_string",
             "spec_verify_last_hip_error")
 
@@ -96,8 +97,10 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_workspace_size.argtypes = [P]
     lib.spec_verify_num_kernels.restype = ctypes.c_int
     lib.spec_verify_num_kernels.argtypes = [P]
-    lib.spec_verify_run.restype = ctypes.c_int
-    lib.spec_verify_run.argtypes = [P, ctypes.POINTER(Args), P]
+    for name in ("spec_verify_run", "spec_verify_run_greedy", "spec_verify_run_point_drafts"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P, ctypes.POINTER(Args), P]
     lib.spec_verify_destroy.restype = ctypes.c_int
     lib.spec_verify_destroy.argtypes = [P]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
@@ -189,12 +192,40 @@ class SpecVerifier:
                  temperature: float, *, num_seqs: Optional[int] = None,
                  total_draft_rows: Optional[int] = None, out: Optional[VerifyOutput] = None,
                  timing_events: Optional[Sequence] = None, stream=None) -> VerifyOutput:
-        """Enqueue one verify step on `stream` (default: torch's current stream).
+        """Enqueue one verify step (spec_verify_run) on `stream` (default:
+        torch's current stream).
 
         num_seqs / total_draft_rows default to the tensor shapes
         (cu_draft has B+1 entries, draft_logits has R_d rows).  Nothing is
         synchronised; `out` (see allocate_outputs) is filled asynchronously.
         """
+        return self._run("spec_verify_run", cu_draft, target_logits, draft_logits,
+                         draft_tokens, uniforms, temperature, num_seqs, total_draft_rows,
+                         out, timing_events, stream)
+
+    def point_drafts(self, cu_draft, target_logits, draft_tokens, uniforms,
+                     temperature: float, *, num_seqs: Optional[int] = None,
+                     out: Optional[VerifyOutput] = None,
+                     timing_events: Optional[Sequence] = None, stream=None) -> VerifyOutput:
+        """Verify deterministic drafts (spec_verify_run_point_drafts): the
+        draft distribution is the point mass at each proposed token; no draft
+        logits.  R_d = draft_tokens.numel()."""
+        return self._run("spec_verify_run_point_drafts", cu_draft, target_logits, None,
+                         draft_tokens, uniforms, temperature, num_seqs,
+                         int(draft_tokens.numel()), out, timing_events, stream)
+
+    def greedy(self, cu_draft, target_logits, draft_tokens, *,
+               num_seqs: Optional[int] = None, out: Optional[VerifyOutput] = None,
+               timing_events: Optional[Sequence] = None, stream=None) -> VerifyOutput:
+        """Greedy verification (spec_verify_run_greedy): argmax of each
+        target row, lowest id on ties.  Only out_tokens, num_accepted and
+        status are written.  R_d = draft_tokens.numel()."""
+        return self._run("spec_verify_run_greedy", cu_draft, target_logits, None,
+                         draft_tokens, None, 1.0, num_seqs, int(draft_tokens.numel()),
+                         out, timing_events, stream)
+
+    def _run(self, entry, cu_draft, target_logits, draft_logits, draft_tokens, uniforms,
+             temperature, num_seqs, total_draft_rows, out, timing_events, stream):
         torch = self._torch
         B = int(cu_draft.shape[0]) - 1 if num_seqs is None else int(num_seqs)
         R_d = int(draft_logits.shape[0]) if (total_draft_rows is None and draft_logits is not None) \
@@ -234,9 +265,9 @@ class SpecVerifier:
             stream = torch.cuda.current_stream(self.device)
         handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
         lib = load_library()
-        st = lib.spec_verify_run(self._ctx, ctypes.byref(a), ctypes.c_void_p(handle))
+        st = getattr(lib, entry)(self._ctx, ctypes.byref(a), ctypes.c_void_p(handle))
         if st != OK:
-            raise SpecVerifyError("spec_verify_run", st, lib.spec_verify_last_hip_error())
+            raise SpecVerifyError(entry, st, lib.spec_verify_last_hip_error())
         self._keepalive = events
         return out
 

@@ -15,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "spec_verify.hip")
 HEADERS = [os.path.join(PKG, "csrc", "spec_verify_kernels.hpp"),
+           os.path.join(PKG, "csrc", "greedy_kernels.hpp"),
            os.path.join(ROOT, "include", "spec_verify.h")]
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libspec_verify.so")

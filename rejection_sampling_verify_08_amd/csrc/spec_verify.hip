@@ -1,6 +1,8 @@
 // spec_verify.hip -- host side of the C ABI declared in include/spec_verify.h:
 // argument checks, workspace layout, and the two launches of one verify step
-// on the caller's HIP stream.  The device code is in spec_verify_kernels.hpp.
+// on the caller's HIP stream.  The device code is in spec_verify_kernels.hpp
+// (sampled verification, with draft logits or point-mass drafts) and
+// greedy_kernels.hpp (greedy verification).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -10,6 +12,7 @@
 
 #include "spec_verify.h"
 #include "spec_verify_kernels.hpp"
+#include "greedy_kernels.hpp"
 
 namespace {
 
@@ -92,14 +95,18 @@ int combine_lanes(int64_t tasks_per_row) {
   return L;
 }
 
-template <int DT, bool VEC, bool CHECK>
-hipError_t launch_all(const spec_verify_ctx* ctx, const spec_verify_args* a,
-                      hipStream_t stream) {
+enum class Mode { kSampled, kPointDrafts, kGreedy };
+
+template <int DT, bool VEC, bool CHECK, int MODE>
+hipError_t launch_sampled(const spec_verify_ctx* ctx, const spec_verify_args* a,
+                          hipStream_t stream) {
   using namespace sv;
   const int64_t B = a->num_seqs;
   const int64_t R_d = a->total_draft_rows;
   const int64_t R_t = R_d + B;
-  const int64_t rows = R_t + R_d;
+  // point-mass drafts have no draft rows to scan
+  const int64_t rows = MODE == kDraftLogits ? R_t + R_d : R_t;
+  const void* draft = MODE == kDraftLogits ? a->draft_logits : nullptr;
   const ExpConsts ec = exp_consts(a->temperature);
   char* ws = static_cast<char*>(a->workspace);
   Partial* partials = reinterpret_cast<Partial*>(ws + ctx->layout.partials);
@@ -108,11 +115,11 @@ hipError_t launch_all(const spec_verify_ctx* ctx, const spec_verify_args* a,
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(a->timing_events);
   hipError_t e;
 
-  // kernel 1: one pass over all target and draft rows
+  // kernel 1: one pass over all target (and draft) rows
   const int64_t grid1 = ceil_div(rows * ctx->tasks_per_row, kStatsWaves);
   if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((row_stats_kernel<DT, VEC, CHECK>), dim3((unsigned)grid1),
-                     dim3(kStatsThreads), 0, stream, a->target_logits, a->draft_logits, R_t,
+                     dim3(kStatsThreads), 0, stream, a->target_logits, draft, R_t,
                      rows, a->ld, ctx->vocab, ctx->tasks_per_row, ec, partials, counters, B,
                      a->status);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -124,8 +131,8 @@ hipError_t launch_all(const spec_verify_ctx* ctx, const spec_verify_args* a,
   if (G < 1) G = 1;
   if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   const size_t lds = (size_t)ctx->num_tiles * sizeof(double);
-  hipLaunchKernelGGL((finish_kernel<DT, VEC, CHECK>), dim3((unsigned)(B * G)), dim3(kThreads),
-                     lds, stream, a->target_logits, a->draft_logits, a->ld, ctx->vocab, R_t,
+  hipLaunchKernelGGL((finish_kernel<DT, VEC, CHECK, MODE>), dim3((unsigned)(B * G)),
+                     dim3(kThreads), lds, stream, a->target_logits, draft, a->ld, ctx->vocab, R_t,
                      R_d, a->cu_draft, a->draft_tokens, a->uniforms, ec, partials,
                      ctx->tasks_per_row, combine_lanes(ctx->tasks_per_row), ctx->num_tiles,
                      (int)G, tiles, counters, a->out_tokens, a->out_num_accepted,
@@ -135,14 +142,99 @@ hipError_t launch_all(const spec_verify_ctx* ctx, const spec_verify_args* a,
   return hipSuccess;
 }
 
+template <int DT, bool VEC, bool CHECK>
+hipError_t launch_greedy(const spec_verify_ctx* ctx, const spec_verify_args* a,
+                         hipStream_t stream) {
+  using namespace sv;
+  const int64_t B = a->num_seqs;
+  const int64_t R_d = a->total_draft_rows;
+  const int64_t R_t = R_d + B;
+  // the argmax partials reuse the row-statistics section of the workspace
+  ArgPartial* partials =
+      reinterpret_cast<ArgPartial*>(static_cast<char*>(a->workspace) + ctx->layout.partials);
+  hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(a->timing_events);
+  hipError_t e;
+  const int64_t grid1 = ceil_div(R_t * ctx->tasks_per_row, kStatsWaves);
+  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((argmax_kernel<DT, VEC, CHECK>), dim3((unsigned)grid1), dim3(kStatsThreads),
+                     0, stream, a->target_logits, R_t, a->ld, ctx->vocab, ctx->tasks_per_row,
+                     partials, a->status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((greedy_finish_kernel<CHECK>), dim3((unsigned)B), dim3(kGreedyThreads), 0,
+                     stream, ctx->vocab, R_t, R_d, a->cu_draft, a->draft_tokens, partials,
+                     ctx->tasks_per_row, combine_lanes(ctx->tasks_per_row), a->out_tokens,
+                     a->out_num_accepted, a->status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+template <int DT, bool VEC, bool CHECK>
+hipError_t launch_mode(const spec_verify_ctx* ctx, const spec_verify_args* a, hipStream_t s,
+                       Mode mode) {
+  switch (mode) {
+    case Mode::kSampled: return launch_sampled<DT, VEC, CHECK, sv::kDraftLogits>(ctx, a, s);
+    case Mode::kPointDrafts: return launch_sampled<DT, VEC, CHECK, sv::kDraftPoint>(ctx, a, s);
+    default: return launch_greedy<DT, VEC, CHECK>(ctx, a, s);
+  }
+}
+
 template <int DT>
 hipError_t dispatch_vec(const spec_verify_ctx* ctx, const spec_verify_args* a,
-                        hipStream_t s, bool vec, bool check) {
-  if (vec) return check ? launch_all<DT, true, true>(ctx, a, s) : launch_all<DT, true, false>(ctx, a, s);
-  return check ? launch_all<DT, false, true>(ctx, a, s) : launch_all<DT, false, false>(ctx, a, s);
+                        hipStream_t s, bool vec, bool check, Mode mode) {
+  if (vec) return check ? launch_mode<DT, true, true>(ctx, a, s, mode)
+                        : launch_mode<DT, true, false>(ctx, a, s, mode);
+  return check ? launch_mode<DT, false, true>(ctx, a, s, mode)
+               : launch_mode<DT, false, false>(ctx, a, s, mode);
 }
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Host-side argument checks shared by the three entry points, then the
+// launches.  Fields a mode does not use are not checked.
+int run_mode(const spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_stream,
+             Mode mode) {
+  if (!ctx || !a) return SPEC_VERIFY_EINVAL;
+  const bool sampled = mode != Mode::kGreedy;
+  const bool draft_rows = mode == Mode::kSampled;
+  const int64_t B = a->num_seqs;
+  const int64_t R_d = a->total_draft_rows;
+  if (B < 0 || R_d < 0) return SPEC_VERIFY_EINVAL;
+  if (sampled && (!(a->temperature > 0.0f) || !std::isfinite(a->temperature)))
+    return SPEC_VERIFY_EINVAL;
+  if (a->ld < ctx->vocab) return SPEC_VERIFY_EINVAL;
+  if (B > ctx->max_seqs || R_d > ctx->max_draft_rows) return SPEC_VERIFY_ECAPACITY;
+  if (B == 0) return SPEC_VERIFY_OK;
+  const size_t esize = ctx->dtype == SPEC_VERIFY_BF16 ? 2 : 4;
+  if (!a->cu_draft || !a->target_logits || !a->out_tokens || !a->out_num_accepted ||
+      !a->workspace)
+    return SPEC_VERIFY_EINVAL;
+  if (sampled && !a->uniforms) return SPEC_VERIFY_EINVAL;
+  if (R_d > 0 && !a->draft_tokens) return SPEC_VERIFY_EINVAL;
+  if (draft_rows && R_d > 0 && !a->draft_logits) return SPEC_VERIFY_EINVAL;
+  const void* draft = draft_rows ? a->draft_logits : nullptr;
+  if (!aligned(a->target_logits, esize) || (draft && !aligned(draft, esize)) ||
+      !aligned(a->cu_draft, 4) || (sampled && !aligned(a->uniforms, 4)) ||
+      !aligned(a->out_tokens, 4) || !aligned(a->out_num_accepted, 4) ||
+      !aligned(a->workspace, kAlign))
+    return SPEC_VERIFY_EINVAL;
+  if (a->workspace_bytes < ctx->layout.total) return SPEC_VERIFY_ECAPACITY;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e);
+  if (cur != ctx->device) return SPEC_VERIFY_EINVAL;
+
+  const bool vec = aligned(a->target_logits, 16) && (R_d == 0 || !draft || aligned(draft, 16)) &&
+                   ((size_t)a->ld * esize) % 16 == 0;
+  const bool check = (ctx->flags & SPEC_VERIFY_FLAG_CHECK) != 0;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  e = ctx->dtype == SPEC_VERIFY_BF16 ? dispatch_vec<1>(ctx, a, s, vec, check, mode)
+                                     : dispatch_vec<0>(ctx, a, s, vec, check, mode);
+  if (e != hipSuccess) return hip_fail(e);
+  return SPEC_VERIFY_OK;
+}
 
 }  // namespace
 
@@ -199,38 +291,17 @@ size_t spec_verify_workspace_size(const spec_verify_ctx* ctx) {
 int spec_verify_num_kernels(const spec_verify_ctx* ctx) { return ctx ? 2 : 0; }
 
 int spec_verify_run(const spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_stream) {
-  if (!ctx || !a) return SPEC_VERIFY_EINVAL;
-  const int64_t B = a->num_seqs;
-  const int64_t R_d = a->total_draft_rows;
-  if (B < 0 || R_d < 0) return SPEC_VERIFY_EINVAL;
-  if (!(a->temperature > 0.0f) || !std::isfinite(a->temperature)) return SPEC_VERIFY_EINVAL;
-  if (a->ld < ctx->vocab) return SPEC_VERIFY_EINVAL;
-  if (B > ctx->max_seqs || R_d > ctx->max_draft_rows) return SPEC_VERIFY_ECAPACITY;
-  if (B == 0) return SPEC_VERIFY_OK;
-  const size_t esize = ctx->dtype == SPEC_VERIFY_BF16 ? 2 : 4;
-  if (!a->cu_draft || !a->target_logits || !a->uniforms || !a->out_tokens ||
-      !a->out_num_accepted || !a->workspace)
-    return SPEC_VERIFY_EINVAL;
-  if (R_d > 0 && (!a->draft_logits || !a->draft_tokens)) return SPEC_VERIFY_EINVAL;
-  if (!aligned(a->target_logits, esize) || (a->draft_logits && !aligned(a->draft_logits, esize)) ||
-      !aligned(a->cu_draft, 4) || !aligned(a->uniforms, 4) || !aligned(a->out_tokens, 4) ||
-      !aligned(a->out_num_accepted, 4) || !aligned(a->workspace, kAlign))
-    return SPEC_VERIFY_EINVAL;
-  if (a->workspace_bytes < ctx->layout.total) return SPEC_VERIFY_ECAPACITY;
-  int cur = -1;
-  hipError_t e = hipGetDevice(&cur);
-  if (e != hipSuccess) return hip_fail(e);
-  if (cur != ctx->device) return SPEC_VERIFY_EINVAL;
+  return run_mode(ctx, a, hip_stream, Mode::kSampled);
+}
 
-  const bool vec = aligned(a->target_logits, 16) &&
-                   (R_d == 0 || aligned(a->draft_logits, 16)) &&
-                   ((size_t)a->ld * esize) % 16 == 0;
-  const bool check = (ctx->flags & SPEC_VERIFY_FLAG_CHECK) != 0;
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  e = ctx->dtype == SPEC_VERIFY_BF16 ? dispatch_vec<1>(ctx, a, s, vec, check)
-                                     : dispatch_vec<0>(ctx, a, s, vec, check);
-  if (e != hipSuccess) return hip_fail(e);
-  return SPEC_VERIFY_OK;
+int spec_verify_run_point_drafts(const spec_verify_ctx* ctx, const spec_verify_args* a,
+                                 void* hip_stream) {
+  return run_mode(ctx, a, hip_stream, Mode::kPointDrafts);
+}
+
+int spec_verify_run_greedy(const spec_verify_ctx* ctx, const spec_verify_args* a,
+                           void* hip_stream) {
+  return run_mode(ctx, a, hip_stream, Mode::kGreedy);
 }
 
 int spec_verify_destroy(spec_verify_ctx* ctx) {

@@ -359,21 +359,35 @@ __device__ __forceinline__ RowNorm combine_rows_packed(const Partial* __restrict
 }
 
 // Final-draw weights of one group, in a common positive scale:
-//   residual: w = max(0, e_p - rho * e_q) = max(0, p - q) * s_p * 2^Kp
-//   bonus   : w = e_p                      = p * s_p * 2^Kp
+//   residual : w = max(0, e_p - rho * e_q) = max(0, p - q) * s_p * 2^Kp
+//   point    : w = e_p, except 0 at token x = max(0, p - delta_x) * s_p * 2^Kp
+//   bonus    : w = e_p                      = p * s_p * 2^Kp
+constexpr int kDrawBonus = 0;
+constexpr int kDrawResidual = 1;   // draft distribution given by draft logits
+constexpr int kDrawPoint = 2;      // draft distribution is the point mass at x
+
 struct DrawConsts {
   float Ap, Aq;          // per-row shifts
   float rho_hi, rho_lo;  // rho = (s_p / s_q) 2^(Kp - Kq), split
-  int residual;          // 1: residual of (p, q); 0: bonus from p
+  int residual;          // kDrawBonus, kDrawResidual or kDrawPoint
+  int64_t x;             // kDrawPoint: the rejected draft token
 };
 
+// rp/rq hold group g of the p and q rows (rq unused unless kDrawResidual);
+// e0 = 8 g is the group's first logit index.
 template <int DT>
 __device__ __forceinline__ void weights_of(const GroupRaw<DT>& rp, const GroupRaw<DT>& rq,
-                                           const DrawConsts& dc, const ExpConsts& ec,
-                                           float w[kGroup]) {
+                                           int64_t e0, const DrawConsts& dc,
+                                           const ExpConsts& ec, float w[kGroup]) {
   float lp[kGroup];
   unpack<DT>(rp, lp);
-  if (dc.residual) {
+  if (dc.residual == kDrawPoint) {
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const float ep = exp_term(lp[k], dc.Ap, ec);
+      w[k] = (e0 + k == dc.x) ? 0.0f : ep;
+    }
+  } else if (dc.residual == kDrawResidual) {
     float lq[kGroup];
     unpack<DT>(rq, lq);
 #pragma unroll
@@ -407,10 +421,21 @@ struct SeqShared {
 
 // ---------------------------------------------------------------- finishing
 
-// One workgroup per sequence (blockIdx = b).  The row partials come from
-// row_stats_kernel, which ran before on the same stream: target row r owns
-// partials [r * tpr, +tpr), draft row d owns [(target_rows + d) * tpr, +tpr).
-template <int DT, bool VEC, bool CHECK>
+// Draft-distribution modes of the finishing kernel.
+//   kDraftLogits: q_i = softmax(draft logits / T) ([A] 1.2, [D] 2.2).
+//   kDraftPoint : the draft proposes tokens without a distribution (n-gram /
+//                 prompt-lookup drafting, [A] 1.4 and 3.3, [D] 4.1), so
+//                 q_i is the point mass at x_i: the test is u < p(x), and
+//                 a rejection draws from max(0, p - delta_x), i.e. p with
+//                 x removed.  No draft row is read.
+constexpr int kDraftLogits = 0;
+constexpr int kDraftPoint = 1;
+
+// G workgroups per sequence (blockIdx = b * G + g).  The row partials come
+// from row_stats_kernel, which ran before on the same stream: target row r
+// owns partials [r * tpr, +tpr), draft row d owns
+// [(target_rows + d) * tpr, +tpr) (kDraftLogits only).
+template <int DT, bool VEC, bool CHECK, int MODE>
 __global__ __launch_bounds__(kThreads) void finish_kernel(
     const void* __restrict__ target, const void* __restrict__ draft, int64_t ld, int64_t V,
     int64_t target_rows, int64_t draft_rows, const int32_t* __restrict__ cu,
@@ -465,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
   int64_t n = gamma;
   for (;; lo += 64) {
     const int64_t hi_t = lo + 64 < gamma + 1 ? lo + 64 : gamma + 1;
-    const int64_t hi_d = lo + 64 < gamma ? lo + 64 : gamma;
+    const int64_t hi_d = lo + 64 < gamma ? lo + 64 : gamma;   // draft positions
     // wave 0 gathers the logits at the draft tokens first; their latency
     // overlaps the combine below
     int32_t x = -1;
@@ -476,11 +501,11 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
       u = uniforms[trow0 + i_me];
       if (x >= 0 && x < V) {
         lpx = load_logit<DT>(row_ptr<DT>(target, trow0 + i_me, ld), x);
-        lqx = load_logit<DT>(row_ptr<DT>(draft, drow0 + i_me, ld), x);
+        if (MODE == kDraftLogits) lqx = load_logit<DT>(row_ptr<DT>(draft, drow0 + i_me, ld), x);
       }
     }
     // combine: rows of this window, rows_per_wave at a time per wave
-    const int64_t nt = hi_t - lo, nd = hi_d - lo;
+    const int64_t nt = hi_t - lo, nd = MODE == kDraftLogits ? hi_d - lo : 0;
     for (int64_t r0 = (int64_t)wave * rows_per_wave; r0 < nt + nd;
          r0 += (int64_t)kWaves * rows_per_wave) {
       const int64_t r = r0 + lane / L;
@@ -502,6 +527,13 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
         double r = 0.0;
         if (x < 0 || x >= V) {
           badtok = true;
+        } else if (MODE == kDraftPoint) {
+          const double Mp = sh.M[0][lane], sp = sh.s[0][lane];
+          // r = p_i(x) / 1
+          r = exp(((double)lpx - Mp) / ec.T) / sp;
+          if (g == 0 && out_p) out_p[drow0 + i_me] = (float)r;
+          if (g == 0 && out_q) out_q[drow0 + i_me] = 1.0f;
+          if (CHECK && Mp == -INFINITY) wbad |= SPEC_VERIFY_DEV_EMPTY_ROW;
         } else {
           const double Mp = sh.M[0][lane], Mq = sh.M[1][lane];
           const double sp = sh.s[0][lane], sq = sh.s[1][lane];
@@ -561,11 +593,17 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
       const int32_t xi = tokens[drow0 + i];
       if (xi < 0 || xi >= V) continue;
       const RowNorm rp = combine_rows_packed(part, tpr, 64, prow_t0 + i, true, ec, lane);
-      const RowNorm rq = combine_rows_packed(part, tpr, 64, prow_d0 + i, true, ec, lane);
       if (lane == 0) {
         const double lp = load_logit<DT>(row_ptr<DT>(target, trow0 + i, ld), xi);
-        const double lq = load_logit<DT>(row_ptr<DT>(draft, drow0 + i, ld), xi);
         if (out_p) out_p[drow0 + i] = (float)(exp((lp - (double)rp.M) / ec.T) / rp.s);
+      }
+      if (MODE == kDraftPoint) {
+        if (lane == 0 && out_q) out_q[drow0 + i] = 1.0f;
+        continue;
+      }
+      const RowNorm rq = combine_rows_packed(part, tpr, 64, prow_d0 + i, true, ec, lane);
+      if (lane == 0) {
+        const double lq = load_logit<DT>(row_ptr<DT>(draft, drow0 + i, ld), xi);
         if (out_q) out_q[drow0 + i] = (float)(exp((lq - (double)rq.M) / ec.T) / rq.s);
       }
     }
@@ -574,15 +612,18 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
   // ---- final-draw weights: residual at n, or the bonus row ([A] 1.2 step 3,
   // [D] 2.2), in the common scale s_p 2^Kp
   const int residual = n < gamma ? 1 : 0;
+  // the draft row is read only for a residual against draft logits
+  const bool read_q = MODE == kDraftLogits && residual;
   const void* prow = row_ptr<DT>(target, trow0 + n, ld);
-  const void* qrow = residual ? row_ptr<DT>(draft, drow0 + n, ld) : prow;
+  const void* qrow = read_q ? row_ptr<DT>(draft, drow0 + n, ld) : prow;
   const float Mp = sh.M[0][n - lo];
   const double sp = sh.s[0][n - lo];
   DrawConsts dc;
-  dc.residual = residual;
+  dc.residual = !residual ? kDrawBonus : (MODE == kDraftPoint ? kDrawPoint : kDrawResidual);
+  dc.x = (MODE == kDraftPoint && residual) ? (int64_t)tokens[drow0 + n] : -1;
   dc.Ap = shift_of(Mp, ec);
   const double Kp = offset_of(Mp, dc.Ap, ec);
-  if (residual) {
+  if (read_q) {
     const float Mq = sh.M[1][n - lo];
     const double sq = sh.s[1][n - lo];
     dc.Aq = shift_of(Mq, ec);
@@ -609,13 +650,13 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
       for (int j = 0; j < kTileGroupsPerLane; ++j) {
         const int64_t gi = t * kTileGroups + j * 64 + lane;   // past V: all -inf
         load_group<DT, VEC>(prow, gi, V, cp[j]);
-        if (residual) load_group<DT, VEC>(qrow, gi, V, cq[j]);
+        if (read_q) load_group<DT, VEC>(qrow, gi, V, cq[j]);
       }
       float lsum = 0.0f;
 #pragma unroll
       for (int j = 0; j < kTileGroupsPerLane; ++j) {
         float w[kGroup];
-        weights_of<DT>(cp[j], cq[j], dc, ec, w);
+        weights_of<DT>(cp[j], cq[j], (t * kTileGroups + j * 64 + lane) * kGroup, dc, ec, w);
         lsum += seq_sum8(w);
       }
       const double ts = wave_xor_sum((double)lsum);
@@ -663,16 +704,17 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     // empty residual (invalid input or extreme rounding): draw from p_n;
     // this wave recomputes every tile sum of the target row alone
     fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
-    dd.residual = 0;
+    dd.residual = kDrawBonus;
     fallback = true;
     total = 0.0;
     for (int64_t t = 0; t < num_tiles; ++t) {
       float lsum = 0.0f;
       for (int j = 0; j < kTileGroupsPerLane; ++j) {
         GroupRaw<DT> r;
-        load_group<DT, VEC>(prow, t * kTileGroups + j * 64 + lane, V, r);
+        const int64_t gi = t * kTileGroups + j * 64 + lane;
+        load_group<DT, VEC>(prow, gi, V, r);
         float w[kGroup];
-        weights_of<DT>(r, r, dd, ec, w);
+        weights_of<DT>(r, r, gi * kGroup, dd, ec, w);
         lsum += seq_sum8(w);
       }
       const double ts = wave_xor_sum((double)lsum);
@@ -705,7 +747,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     for (int j = 0; j < kTileGroupsPerLane; ++j) {
       const int64_t gi = tau * kTileGroups + j * 64 + lane;
       load_group<DT, VEC>(prow, gi, V, rp[j]);
-      if (dd.residual) load_group<DT, VEC>(qrow, gi, V, rq[j]);
+      if (MODE == kDraftLogits && dd.residual == kDrawResidual)
+        load_group<DT, VEC>(qrow, gi, V, rq[j]);
     }
     // the four 64-lane scans are independent; their totals chain in order.
     // The weights are recomputed for the search (same code, same values)
@@ -714,16 +757,16 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
 #pragma unroll
     for (int j = 0; j < kTileGroupsPerLane; ++j) {
       float w[kGroup];
-      weights_of<DT>(rp[j], rq[j], dd, ec, w);
+      weights_of<DT>(rp[j], rq[j], (tau * kTileGroups + j * 64 + lane) * kGroup, dd, ec, w);
       incl[j] = wave_incl_scan((double)seq_sum8(w), lane);
     }
     double run = P_excl;
     int64_t last_pos = -1;
 #pragma unroll
     for (int j = 0; j < kTileGroupsPerLane; ++j) {
-      float w[kGroup];
-      weights_of<DT>(rp[j], rq[j], dd, ec, w);
       const int64_t gi = tau * kTileGroups + j * 64 + lane;
+      float w[kGroup];
+      weights_of<DT>(rp[j], rq[j], gi * kGroup, dd, ec, w);
       const double below = __shfl_up(incl[j], 1);
       const double excl = lane == 0 ? 0.0 : below;
       int k_hit = -1;

@@ -85,12 +85,25 @@ class HostOutput:
     status: int
 
 
-def run_gpu(inp: W.VerifyInputs, sv=None, dev_inputs=None, check=False, **kw) -> HostOutput:
+def run_gpu(inp: W.VerifyInputs, sv=None, dev_inputs=None, check=False, mode="sampled",
+            **kw) -> HostOutput:
+    """Run one entry point on `inp`: mode "sampled" (spec_verify_run),
+    "point" (spec_verify_run_point_drafts) or "greedy"
+    (spec_verify_run_greedy).  Outputs a mode does not write read back as
+    whatever allocate_outputs left there."""
     import torch
     sv = sv or make_verifier(inp, check=check)
     d = dev_inputs or to_device(inp, **kw)
-    out = sv(d.cu, d.target, d.draft, d.tokens, d.uniforms, inp.temperature,
-             num_seqs=inp.num_seqs, total_draft_rows=inp.draft_rows)
+    if mode == "sampled":
+        out = sv(d.cu, d.target, d.draft, d.tokens, d.uniforms, inp.temperature,
+                 num_seqs=inp.num_seqs, total_draft_rows=inp.draft_rows)
+    elif mode == "point":
+        out = sv.point_drafts(d.cu, d.target, d.tokens, d.uniforms, inp.temperature,
+                              num_seqs=inp.num_seqs)
+    elif mode == "greedy":
+        out = sv.greedy(d.cu, d.target, d.tokens, num_seqs=inp.num_seqs)
+    else:
+        raise ValueError(mode)
     torch.cuda.synchronize()
     return HostOutput(out.out_tokens.cpu().numpy(), out.num_accepted.cpu().numpy(),
                       out.p_draft.cpu().numpy().astype(np.float64),
@@ -99,11 +112,15 @@ def run_gpu(inp: W.VerifyInputs, sv=None, dev_inputs=None, check=False, **kw) ->
                       int(out.status.cpu().numpy()[0]) & 0xFFFFFFFF)
 
 
-def _final_cdf(inp: W.VerifyInputs, b: int, n: int):
-    """Normalised CDF of the oracle's final-draw weights at position n."""
+def _final_cdf(inp: W.VerifyInputs, b: int, n: int, point: bool = False):
+    """Normalised CDF of the oracle's final-draw weights at position n
+    (point: the draft distribution is the point mass at the draft token)."""
     g = int(inp.gammas[b])
     p = oracle.row_softmax(inp.target_logits[inp.target_row(b, n)], inp.temperature, inp.dtype)
-    if n < g:
+    if n < g and point:
+        w = p.copy()
+        w[int(inp.draft_tokens[inp.draft_row(b, n)])] = 0.0
+    elif n < g:
         q = oracle.row_softmax(inp.draft_logits[inp.draft_row(b, n)], inp.temperature,
                                inp.dtype)
         w = np.maximum(p - q, 0.0)
@@ -123,7 +140,7 @@ class ParityReport:
 
 
 def compare(inp: W.VerifyInputs, gpu: HostOutput, ora, *, label: str = "",
-            check_probs: bool = True) -> ParityReport:
+            check_probs: bool = True, point: bool = False) -> ParityReport:
     B = inp.num_seqs
     cu = inp.cu_draft
     bad = []
@@ -151,7 +168,7 @@ def compare(inp: W.VerifyInputs, gpu: HostOutput, ora, *, label: str = "",
                 bad.append((b, "accept decision differs away from a tie", gn, on))
             continue
         # same count, different drawn token: it must sit at the final-draw tie
-        w, C = _final_cdf(inp, b, gn)
+        w, C = _final_cdf(inp, b, gn, point)
         k = int(gt[gn])
         u = float(inp.uniforms[t0 + g])
         lo = C[k - 1] if k > 0 else 0.0
@@ -182,3 +199,27 @@ def compare(inp: W.VerifyInputs, gpu: HostOutput, ora, *, label: str = "",
     log(f"[parity] {label}: seqs={B} flagged={flagged} tie_diffs={tie_diffs} "
         f"max_prob_rel={max_prob_rel:.3g} max_residual_rel={max_res_rel:.3g}")
     return rep
+
+
+def compare_greedy(inp: W.VerifyInputs, gpu: HostOutput, ora, *, label: str = "") -> None:
+    """Greedy verification is integer work: bit-exact counts and tokens."""
+    R_t = inp.target_rows
+    bad = np.nonzero(gpu.num_accepted != ora.num_accepted)[0]
+    assert bad.size == 0, f"{label}: num_accepted differs at {bad[:5].tolist()}"
+    diff = np.nonzero(gpu.out_tokens[:R_t] != ora.out_tokens[:R_t])[0]
+    assert diff.size == 0, (f"{label}: out_tokens differ at rows {diff[:5].tolist()}: "
+                            f"{gpu.out_tokens[diff[:5]].tolist()} vs "
+                            f"{ora.out_tokens[diff[:5]].tolist()}")
+    log(f"[parity] {label}: seqs={inp.num_seqs} greedy bit-exact, "
+        f"mean accepted {float(ora.num_accepted.mean()):.3f}")
+
+
+def oracle_greedy(inp: W.VerifyInputs):
+    return oracle.verify_greedy(inp.num_seqs, inp.cu_draft, inp.target_logits,
+                                inp.draft_tokens, vocab=inp.vocab, dtype=inp.dtype)
+
+
+def oracle_point(inp: W.VerifyInputs):
+    return oracle.verify_onehot(inp.num_seqs, inp.cu_draft, inp.target_logits,
+                                inp.draft_tokens, inp.uniforms, inp.temperature,
+                                vocab=inp.vocab, dtype=inp.dtype)

@@ -83,6 +83,8 @@ def test_host_side_argument_checks_without_a_device():
     assert lib.spec_verify_create(bc(ctx), 0, 1000, 1, 1, -1, 0, bc(ws)) == binding.EINVAL
     assert lib.spec_verify_create(bc(ctx), 0, 1000, 1, 1, 1, 0x80, bc(ws)) == binding.EINVAL
     assert lib.spec_verify_run(None, None, None) == binding.EINVAL
+    assert lib.spec_verify_run_greedy(None, None, None) == binding.EINVAL
+    assert lib.spec_verify_run_point_drafts(None, None, None) == binding.EINVAL
     assert lib.spec_verify_destroy(None) == binding.OK
     assert lib.spec_verify_workspace_size(None) == 0
     assert lib.spec_verify_num_kernels(None) == 0

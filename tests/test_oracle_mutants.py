@@ -1,10 +1,12 @@
 """The oracle's pins must catch plausible mistakes.
 
 Each case copies oracle.c, plants one mistake (a transposed operand, a wrong
-sign, index or comparison, a dropped term, a missing stop), builds the mutant
-with gcc into a temporary directory and runs the fast pins of
-test_oracle_pins.py against it.  At least one pin must fail for every mutant.
-Everything runs on the CPU; the real oracle library is restored afterwards.
+sign, index or comparison, a dropped term, a missing stop) inside one
+function, builds the mutant with gcc into a temporary directory and runs that
+function's fast pins (test_oracle_pins.py for the sampled verify,
+test_oracle_pins_modes.py for greedy and point-mass drafts) against it.  At
+least one pin must fail for every mutant.  Everything runs on the CPU; the
+real oracle library is restored afterwards.
 """
 import os
 import subprocess
@@ -13,6 +15,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_pins as pins
+from tests import test_oracle_pins_modes as mpins
 
 MUTANTS = [
     ("accept test in the wrong direction",
@@ -44,6 +47,44 @@ MUTANTS = [
      "out_num_accepted[b] = (int32_t)j;", "out_num_accepted[b] = (int32_t)(j + 1);"),
 ]
 
+SAMPLED = "int oracle_verify("
+GREEDY = "int oracle_verify_greedy("
+POINT = "int oracle_verify_onehot("
+
+MODE_MUTANTS = [
+    ("greedy: ties go to the highest id", None,
+     "if (v > bv) { bv = v; best = k; }", "if (v >= bv) { bv = v; best = k; }"),
+    ("greedy: no stop at the first mismatch", GREEDY,
+     "{ j = i; break; }", "{ j = i; }"),
+    ("greedy: mismatch emits the previous row's argmax", GREEDY,
+     "else if (i == j) v = (int32_t)row_argmax(target_logits, dtype, trow0 + j, ld, vocab);",
+     "else if (i == j) v = (int32_t)row_argmax(target_logits, dtype, trow0 + (j > 0 ? j - 1 : 0), ld, vocab);"),
+    ("greedy: target rows without the per-sequence offset", GREEDY,
+     "const int64_t trow0 = (int64_t)cu_draft[b] + b;", "const int64_t trow0 = (int64_t)cu_draft[b];"),
+    ("point: rejected token kept in the residual", POINT,
+     "const double q = (k == draft_tokens[drow0 + j]) ? 1.0 : 0.0;", "const double q = 0.0;"),
+    ("point: accept test not strict", POINT,
+     "if (!(u < px)) { j = i; break; }", "if (!(u <= px)) { j = i; break; }"),
+    ("point: accept test against 1 - p(x)", POINT,
+     "if (!(u < px)) { j = i; break; }", "if (!(u < 1.0 - px)) { j = i; break; }"),
+    ("point: residual drawn from the next row", POINT,
+     "const int64_t tj = trow0 + j;", "const int64_t tj = trow0 + (j < gamma ? j + 1 : j);"),
+    ("point: final draw uses the stopping position's uniform", POINT,
+     "const double u = (double)uniforms[trow0 + gamma];",
+     "const double u = (double)uniforms[trow0 + j];"),
+]
+
+MODE_PINS = [
+    (mpins.test_greedy_golden_cases, {}),
+    (mpins.test_greedy_argmax_is_numpy_first_occurrence, dict(dtype="bf16")),
+    (mpins.test_greedy_is_the_zero_temperature_limit_of_sampled_verify, {}),
+    (mpins.test_point_draft_golden_cases, {}),
+    (mpins.test_point_drafts_equal_sampled_verify_with_point_mass_q, dict(dtype="bf16", T=0.7)),
+    (mpins.test_point_draft_accept_threshold_is_p_of_x, {}),
+    (mpins.test_point_draft_output_law_by_grid_count, {}),
+    (mpins.test_point_draft_edge_cases, {}),
+]
+
 FAST_PINS = [
     (pins.test_row_softmax_matches_scipy, dict(dtype="f32", T=0.7)),
     (pins.test_row_softmax_closed_forms, {}),
@@ -62,11 +103,26 @@ FAST_PINS = [
 ]
 
 
-def _build_mutant(tmp_path, old, new):
+def _build_mutant(tmp_path, old, new, scope=SAMPLED):
+    """Replace `old` (which must occur exactly once in the body of the
+    function that starts with `scope`) by `new`."""
     src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
-    assert src.count(old) == 1, f"mutation site not unique: {old!r}"
+    if scope is None:                       # a site unique in the whole file
+        assert src.count(old) == 1, f"mutation site not unique: {old!r}"
+        path = tmp_path / "oracle_mutant.c"
+        path.write_text(src.replace(old, new))
+        return _compile(tmp_path, path)
+    start = src.index(scope)
+    end = src.find("\nint oracle_", start + 1)
+    end = len(src) if end < 0 else end
+    body = src[start:end]
+    assert body.count(old) == 1, f"mutation site not unique in {scope}: {old!r}"
     path = tmp_path / "oracle_mutant.c"
-    path.write_text(src.replace(old, new))
+    path.write_text(src[:start] + body.replace(old, new) + src[end:])
+    return _compile(tmp_path, path)
+
+
+def _compile(tmp_path, path):
     lib = tmp_path / "liboracle_mutant.so"
     subprocess.run(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC",
                     "-shared", "-o", str(lib), str(path), "-lm"], check=True)
@@ -76,14 +132,28 @@ def _build_mutant(tmp_path, old, new):
 @pytest.mark.slow
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(tmp_path, monkeypatch, name, old, new):
-    lib = _build_mutant(tmp_path, old, new)
+    # helper-function sites are unique in the file; sites inside the sampled
+    # verify function are looked up in its body
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    lib = _build_mutant(tmp_path, old, new, None if src.count(old) == 1 else SAMPLED)
+    _expect_caught(monkeypatch, lib, FAST_PINS, name)
+
+
+def _expect_caught(monkeypatch, lib, pin_list, name):
     monkeypatch.setattr(oracle, "LIB_PATH", lib)
     monkeypatch.setattr(oracle, "_lib", None)
     caught = []
-    for fn, kw in FAST_PINS:
+    for fn, kw in pin_list:
         try:
             fn(oracle, **kw)
         except (AssertionError, ValueError, IndexError):
             caught.append(fn.__name__)
     monkeypatch.setattr(oracle, "_lib", None)
     assert caught, f"no pin caught the mutant: {name}"
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,scope,old,new", MODE_MUTANTS, ids=[m[0] for m in MODE_MUTANTS])
+def test_mode_pins_catch_mutant(tmp_path, monkeypatch, name, scope, old, new):
+    lib = _build_mutant(tmp_path, old, new, scope)
+    _expect_caught(monkeypatch, lib, MODE_PINS, name)

@@ -80,7 +80,8 @@ class VerifyInputs:
 
     @property
     def draft_rows(self) -> int:
-        return int(self.draft_logits.shape[0])
+        """R_d = cu_draft[B] (also when no draft logits are stored)."""
+        return int(self.cu_draft[-1])
 
     def target_row(self, b: int, i: int) -> int:
         return int(self.cu_draft[b]) + b + i
@@ -268,6 +269,24 @@ def build(name: str, seed: int, gammas, vocab: int, dtype: str,
                         gammas=gammas, cu_draft=cu, target_logits=tgt,
                         draft_logits=dft, draft_tokens=tokens,
                         uniforms=uniforms)
+
+
+def with_deterministic_drafts(inp: VerifyInputs, name: Optional[str] = None) -> VerifyInputs:
+    """A copy of `inp` whose draft tokens are proposed without sampling.
+
+    Each draft token becomes the first maximum of its draft row: the draft
+    model decoding greedily, which is the temperature -> 0 limit of the
+    Gumbel-max draw above.  These are the inputs of greedy verification and
+    stand in for drafts that carry no distribution at all (n-gram /
+    prompt-lookup proposals, "推测解码与连续批处理深度实战" sections 1.4 and
+    3.3).  Target rows, draft rows and uniforms are shared with `inp`.
+    """
+    tokens = np.empty(inp.draft_rows, dtype=np.int32)
+    for r0 in range(0, inp.draft_rows, 64):
+        rows = to_f64(inp.draft_logits[r0:r0 + 64], inp.dtype)
+        tokens[r0:r0 + 64] = np.argmax(rows, axis=1)
+    return dataclasses.replace(inp, name=name or inp.name + " deterministic drafts",
+                               draft_tokens=tokens)
 
 
 # ---------------------------------------------------------------- named workloads
