@@ -125,10 +125,12 @@ hipError_t launch_sampled(const spec_verify_ctx* ctx, const spec_verify_args* a,
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
 
-  // kernel 2: G workgroups per sequence, about one per compute unit in all
+  // kernel 2: G workgroups per sequence, about one per compute unit in all,
+  // sharing a residual's second pass over its rows.  Point-mass drafts never
+  // make that pass (their draws use the row pass's task sums): one each.
   int64_t G = ctx->cu_count / B;
   if (G > ctx->num_tiles) G = ctx->num_tiles;
-  if (G < 1) G = 1;
+  if (G < 1 || MODE == kDraftPoint) G = 1;
   if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   const size_t lds = (size_t)ctx->num_tiles * sizeof(double);
   hipLaunchKernelGGL((finish_kernel<DT, VEC, CHECK, MODE>), dim3((unsigned)(B * G)),

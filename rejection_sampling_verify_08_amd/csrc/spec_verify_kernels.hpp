@@ -31,13 +31,17 @@
 //     the partials into exact row maxima M and normalisers s in double,
 //     evaluates r_i = p_i(x_i) / q_i(x_i) in double, and takes n_b as the
 //     lowest lane of a wave ballot of !(u_i < r_i) ([A] 1.2 step 3, [D] 2.1:
-//     the first rejection ends the test).  Then the G workgroups share one
-//     more read of the final-draw row(s) -- the rejected target/draft pair
-//     or the bonus target row -- computing w_k = max(0, p_k - q_k) (or p_k)
-//     in a common positive scale and one double per 2048-logit tile.  The
+//     the first rejection ends the test).  A residual w_k = max(0, p_k - q_k)
+//     needs both rows again: the G workgroups share one more read of the
+//     rejected target/draft pair, one double per 2048-logit tile, and the
 //     last workgroup to arrive (an integer counter cleared by the row pass)
-//     has one wave scan the tile sums, find the tile holding t = u * S,
-//     re-scan it and write the token: the smallest k with C_k > t.
+//     scans the tile sums for the tile holding t = u * S.  A bonus draw
+//     (w_k = p_k) and a point-mass residual (p with x removed) need no
+//     second pass: the row pass's task sums, moved into the draw's scale,
+//     locate the 4096-logit task holding t (the task holding x is summed
+//     again without it).  Either way the workgroup's 512 threads then search
+//     the one interval in parallel (one group of 8 logits each) and write
+//     the token: the smallest k with C_k > t.
 
 // Determinism: every floating-point reduction has a fixed order; the same
 // device function produces w_k in the tile pass and in the re-scan, and the
@@ -315,6 +319,34 @@ struct RowNorm {
   double s;      // sum_k 2^((l_k - M) log2(e)/T), in double
 };
 
+// One partial per lane: lane slot `sub` of row `row` (an empty partial when
+// inactive or past the row's partials).
+__device__ __forceinline__ Partial load_partial(const Partial* __restrict__ part, int64_t tpr,
+                                                int64_t row, int sub, bool active) {
+  Partial p;
+  p.m = -INFINITY;
+  p.pad = 0.0f;
+  p.s = 0.0;
+  if (active && sub < tpr) p = part[row * tpr + sub];
+  return p;
+}
+
+// Row maximum and normaliser from one partial per lane, L lanes per row.
+__device__ __forceinline__ RowNorm reduce_partials(const Partial& p, int L, const ExpConsts& ec) {
+  float M = p.m;
+  for (int o = L >> 1; o > 0; o >>= 1) M = fmax_nan_ignoring(M, __shfl_xor(M, o));
+  double s = 0.0;
+  if (p.m != -INFINITY) {
+    const double K = offset_of(p.m, shift_of(p.m, ec), ec);
+    s = p.s * exp2(((double)p.m - (double)M) * ec.c64 - K);
+  }
+  for (int o = L >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  RowNorm r;
+  r.M = M;
+  r.s = s;
+  return r;
+}
+
 // Combine rows r0, r0 + 1, ... of a sequence's partial table, `L` lanes per
 // row (L a power of two >= the partials per row, or 64 with a loop when a
 // row has more), so one wave combines 64 / L rows at once.
@@ -414,10 +446,236 @@ __device__ __forceinline__ float seq_sum8(const float w[kGroup]) {
 struct SeqShared {
   float M[2][64];        // row maxima of the current 64-position window
   double s[2][64];       // (0: target rows, 1: draft rows)
+  int32_t x[64];         // draft tokens of the current window
   int n;                 // accepted count
   int skip;              // nonzero: a bad draft token, the sequence is skipped
   uint32_t bad;
 };
+
+// ---------------------------------------------------------------- the draw
+
+struct DrawShared {
+  double wave_tot[kWaves];   // block scan: per-wave group-sum totals
+  int64_t cand[kWaves];      // block search: per-wave first hit (or -1)
+  int64_t last_pos[kWaves];  // block search: per-wave last positive weight
+  double red[kWaves];        // block reduction
+  double total, tt, p_excl;  // the draw's total, u * total, mass before tau
+  int64_t tau;               // the tile / task holding tt
+  int empty;                 // the residual summed to 0
+  int last_wg;               // this workgroup arrived last
+};
+
+// Sum of v[0..n) in a fixed order (64-lane chunks, inclusive scans), one wave.
+__device__ __forceinline__ double wave_total(const double* v, int64_t n, int lane) {
+  double total = 0.0;
+  for (int64_t c = 0; c < n; c += 64) {
+    const double x = (c + lane < n) ? v[c + lane] : 0.0;
+    total += __shfl(wave_incl_scan(x, lane), 63);
+  }
+  return total;
+}
+
+// One wave: the first c with (sum of v[0..c]) > tt; writes ds.tau and
+// ds.p_excl (the sum before it).  tt < total is assumed; rounding can leave
+// no hit, then tau is the last c with v[c] > 0.
+__device__ __forceinline__ void find_interval(const double* v, int64_t n, double tt, int lane,
+                                              DrawShared& ds) {
+  double base = 0.0, p_excl = 0.0;
+  int64_t tau = -1;
+  for (int64_t c = 0; c < n && tau < 0; c += 64) {
+    const double x = (c + lane < n) ? v[c + lane] : 0.0;
+    const double incl = base + wave_incl_scan(x, lane);
+    const uint64_t hit = __ballot(c + lane < n && incl > tt);
+    const double below = __shfl_up(incl, 1);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      tau = c + l;
+      p_excl = __shfl(lane == 0 ? base : below, l);
+    }
+    base = __shfl(incl, 63);
+  }
+  if (tau < 0) {
+    // t at or past the rounded total: the last interval with mass
+    int64_t lastc = -1;
+    double before = 0.0, run = 0.0;
+    for (int64_t c = 0; c < n; ++c) {
+      if (v[c] > 0.0) {
+        lastc = c;
+        before = run;
+      }
+      run += v[c];
+    }
+    tau = lastc;
+    p_excl = before;
+  }
+  if (lane == 0) {
+    ds.tau = tau;
+    ds.p_excl = p_excl;
+  }
+}
+
+// Block-wide search inside one interval of consecutive groups: thread t of
+// the workgroup holds group gi (active threads form a prefix in ascending
+// group order).  The running sum of the weights, starting at p_excl,
+// crosses tt at the returned logit index: the smallest k with C_k > tt (a
+// zero-weight logit is never returned).  If rounding leaves tt past the
+// interval's last weight, the last positive-weight logit is returned.  All
+// threads of the workgroup must call it; the result is valid in every
+// thread.
+template <int DT>
+__device__ __forceinline__ int64_t block_search(const GroupRaw<DT>& rp, const GroupRaw<DT>& rq,
+                                                int64_t gi, bool active, const DrawConsts& dd,
+                                                const ExpConsts& ec, double tt, double p_excl,
+                                                DrawShared& ds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  float w[kGroup];
+  if (active) {
+    weights_of<DT>(rp, rq, gi * kGroup, dd, ec, w);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) w[k] = 0.0f;
+  }
+  const double gs = (double)seq_sum8(w);
+  const double incl = wave_incl_scan(gs, lane);
+  const double below = __shfl_up(incl, 1);
+  if (lane == 63) ds.wave_tot[wave] = incl;
+  __syncthreads();
+  double base = p_excl;
+  for (int v = 0; v < wave; ++v) base += ds.wave_tot[v];
+  const double excl = lane == 0 ? 0.0 : below;
+  int k_hit = -1;
+  int64_t last_pos = -1;
+  float c = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kGroup; ++k) {
+    c += w[k];
+    if (k_hit < 0 && w[k] > 0.0f && base + (excl + (double)c) > tt) k_hit = k;
+    if (w[k] > 0.0f) last_pos = gi * kGroup + k;
+  }
+  const uint64_t hit = __ballot(k_hit >= 0);
+  int64_t cand = -1;
+  if (hit) {
+    const int l = __builtin_ctzll(hit);
+    cand = (gi - lane + l) * kGroup + __shfl(k_hit, l);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int64_t ol = __shfl_xor(last_pos, o);
+    last_pos = ol > last_pos ? ol : last_pos;
+  }
+  if (lane == 0) {
+    ds.cand[wave] = cand;
+    ds.last_pos[wave] = last_pos;
+  }
+  __syncthreads();
+  int64_t token = -1, lp = -1;
+  for (int v = 0; v < kWaves; ++v) {
+    if (token < 0 && ds.cand[v] >= 0) token = ds.cand[v];
+    lp = ds.last_pos[v] > lp ? ds.last_pos[v] : lp;
+  }
+  return token >= 0 ? token : lp;
+}
+
+// Block-wide sum of one double per thread in a fixed order.
+__device__ __forceinline__ double block_sum(double v, DrawShared& ds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const double ws = __shfl(wave_incl_scan(v, lane), 63);
+  if (lane == 0) ds.red[wave] = ws;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < kWaves; ++i) t += ds.red[i];
+  return t;
+}
+
+// Draw from weights that need no second pass over the rows: the bonus
+// (w = e_p) and the point-mass residual (w = e_p with x removed).  The
+// interval sums are the row pass's task sums (4096 logits each) moved into
+// the draw's scale: a task with maximum m summed 2^(l c + A_m), and the draw
+// uses 2^(l c + Ap), so its sum is s_task 2^(Ap - A_m).  The task holding x
+// is summed again here without x (never by subtraction, which would cancel
+// when x dominates it).  One task (512 groups, one per thread of the first
+// 512) is then searched.  `part` points at the row's task partials; task_sum has room for
+// tpr doubles.  Returns the token; `total` receives the weights' sum.
+template <int DT, bool VEC>
+__device__ __forceinline__ int64_t draw_from_task_sums(
+    const Partial* __restrict__ part, int64_t tpr, const void* prow, int64_t V,
+    DrawConsts dc, const ExpConsts& ec, float u_final, double* task_sum, DrawShared& ds,
+    uint32_t& fbad, double& total) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  constexpr int64_t kTaskGroups = kWaveTaskElems / kGroup;   // 512
+  static_assert(kTaskGroups <= kThreads, "one group per thread in a task");
+  const bool point = dc.residual == kDrawPoint;
+  const int64_t xtask = point ? dc.x / kWaveTaskElems : -1;
+  const bool active = tid < kTaskGroups;
+  // issue the partial loads and the x-task's groups together
+  for (int64_t c = tid; c < tpr; c += kThreads) {
+    const Partial pc = part[c];
+    task_sum[c] = (pc.m == -INFINITY)
+                      ? 0.0
+                      : pc.s * exp2((double)dc.Ap - (double)shift_of(pc.m, ec));
+  }
+  GroupRaw<DT> rp;
+  int64_t gi = xtask * kTaskGroups + tid;
+  double xsum = 0.0;
+  if (point) {
+    double gsum = 0.0;
+    if (active) {
+      load_group<DT, VEC>(prow, gi, V, rp);
+      float w[kGroup];
+      weights_of<DT>(rp, rp, gi * kGroup, dc, ec, w);
+      gsum = (double)seq_sum8(w);
+    }
+    xsum = block_sum(gsum, ds);                   // has a barrier
+  }
+  __syncthreads();
+  double xtask_bonus = 0.0;
+  if (point && tid == 0) {
+    xtask_bonus = task_sum[xtask];
+    task_sum[xtask] = xsum;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const double tot = wave_total(task_sum, tpr, lane);
+    if (lane == 0) {
+      ds.total = tot;
+      ds.empty = point && !(tot > 0.0);
+    }
+  }
+  __syncthreads();
+  if (ds.empty) {
+    // empty residual (invalid input or extreme rounding): draw from p
+    fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
+    dc.residual = kDrawBonus;
+    if (tid == 0) task_sum[xtask] = xtask_bonus;
+    __syncthreads();
+    if (wave == 0) {
+      const double tot = wave_total(task_sum, tpr, lane);
+      if (lane == 0) ds.total = tot;
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+    const double tt = (double)u_final * ds.total;
+    find_interval(task_sum, tpr, tt, lane, ds);
+    if (lane == 0) ds.tt = tt;
+  }
+  __syncthreads();
+  total = ds.total;
+  const int64_t tau = ds.tau;
+  if (tau < 0) return -1;                      // no mass at all (invalid row)
+  if (tau != xtask) {
+    gi = tau * kTaskGroups + tid;
+    if (active) load_group<DT, VEC>(prow, gi, V, rp);
+  }
+  const double tt = ds.tt, p_excl = ds.p_excl;
+  __syncthreads();                             // ds.wave_tot etc. are reused
+  return block_search<DT>(rp, rp, gi, active, dc, ec, tt, p_excl, ds);
+}
 
 // ---------------------------------------------------------------- finishing
 
@@ -506,17 +764,36 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     }
     // combine: rows of this window, rows_per_wave at a time per wave
     const int64_t nt = hi_t - lo, nd = MODE == kDraftLogits ? hi_d - lo : 0;
-    for (int64_t r0 = (int64_t)wave * rows_per_wave; r0 < nt + nd;
-         r0 += (int64_t)kWaves * rows_per_wave) {
-      const int64_t r = r0 + lane / L;
-      const bool active = (lane / L) < rows_per_wave && r < nt + nd;
-      const bool is_t = r < nt;
-      const int64_t j = is_t ? prow_t0 + lo + r : prow_d0 + lo + (r - nt);
-      const RowNorm rn = combine_rows_packed(part, tpr, L, j, active, ec, lane);
+    auto store_row = [&](int64_t r, bool active, const RowNorm& rn) {
       if (active && (lane & (L - 1)) == 0) {
+        const bool is_t = r < nt;
         const int64_t i = is_t ? r : r - nt;
         sh.M[is_t ? 0 : 1][i] = rn.M;
         sh.s[is_t ? 0 : 1][i] = rn.s;
+      }
+    };
+    auto table_row = [&](int64_t r) -> int64_t {
+      return r < nt ? prow_t0 + lo + r : prow_d0 + lo + (r - nt);
+    };
+    const int64_t stride = (int64_t)kWaves * rows_per_wave;
+    if (tpr <= L) {
+      // one partial per lane; two passes' loads are issued before either
+      // is reduced (a 64-position window with gamma up to 16 needs two)
+      for (int64_t r0 = (int64_t)wave * rows_per_wave; r0 < nt + nd; r0 += 2 * stride) {
+        const int64_t ra = r0 + lane / L, rb = ra + stride;
+        const bool act_a = (lane / L) < rows_per_wave && ra < nt + nd;
+        const bool act_b = (lane / L) < rows_per_wave && rb < nt + nd;
+        const Partial pa = load_partial(part, tpr, act_a ? table_row(ra) : 0, lane & (L - 1), act_a);
+        const Partial pb = load_partial(part, tpr, act_b ? table_row(rb) : 0, lane & (L - 1), act_b);
+        store_row(ra, act_a, reduce_partials(pa, L, ec));
+        store_row(rb, act_b, reduce_partials(pb, L, ec));
+      }
+    } else {
+      for (int64_t r0 = (int64_t)wave * rows_per_wave; r0 < nt + nd; r0 += stride) {
+        const int64_t r = r0 + lane / L;
+        const bool active = (lane / L) < rows_per_wave && r < nt + nd;
+        store_row(r, active, combine_rows_packed(part, tpr, L, active ? table_row(r) : 0,
+                                                 active, ec, lane));
       }
     }
     __syncthreads();
@@ -555,6 +832,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
       const uint64_t mask = __ballot(reject);
       const uint64_t btok = __ballot(badtok);
       wbad = wave_or(wbad);
+      sh.x[lane] = x;
       if (lane == 0) {
         sh.bad |= wbad;
         if (btok) sh.skip = 1;
@@ -580,9 +858,11 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
 
   // ---- emit the accepted prefix ([B] 流程编排: keep the drafts before the
   // first mismatch); slot n is written by the draw below.
+  // The last window's drafts are in LDS; earlier windows (gamma > 64 only)
+  // are read again.
   if (g == 0) {
     for (int64_t i = tid; i <= gamma; i += kThreads) {
-      if (i < n) out_tokens[trow0 + i] = tokens[drow0 + i];
+      if (i < n) out_tokens[trow0 + i] = i >= lo ? sh.x[i - lo] : tokens[drow0 + i];
       else if (i > n) out_tokens[trow0 + i] = -1;
     }
     if (tid == 0) out_num_accepted[b] = (int32_t)n;
@@ -609,21 +889,22 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     }
   }
 
-  // ---- final-draw weights: residual at n, or the bonus row ([A] 1.2 step 3,
-  // [D] 2.2), in the common scale s_p 2^Kp
+  // ---- final draw ([A] 1.2 step 3, [D] 2.2), in the common scale s_p 2^Kp:
+  // the residual at n, or the bonus from the last target row.
   const int residual = n < gamma ? 1 : 0;
-  // the draft row is read only for a residual against draft logits
-  const bool read_q = MODE == kDraftLogits && residual;
+  // Only a residual against draft logits needs a second pass over its rows;
+  // bonus draws and point-mass residuals draw from the row-pass task sums.
+  const bool tile_pass = MODE == kDraftLogits && residual;
   const void* prow = row_ptr<DT>(target, trow0 + n, ld);
-  const void* qrow = read_q ? row_ptr<DT>(draft, drow0 + n, ld) : prow;
+  const void* qrow = tile_pass ? row_ptr<DT>(draft, drow0 + n, ld) : prow;
   const float Mp = sh.M[0][n - lo];
   const double sp = sh.s[0][n - lo];
   DrawConsts dc;
   dc.residual = !residual ? kDrawBonus : (MODE == kDraftPoint ? kDrawPoint : kDrawResidual);
-  dc.x = (MODE == kDraftPoint && residual) ? (int64_t)tokens[drow0 + n] : -1;
+  dc.x = (MODE == kDraftPoint && residual) ? (int64_t)sh.x[n - lo] : -1;
   dc.Ap = shift_of(Mp, ec);
   const double Kp = offset_of(Mp, dc.Ap, ec);
-  if (read_q) {
+  if (tile_pass) {
     const float Mq = sh.M[1][n - lo];
     const double sq = sh.s[1][n - lo];
     dc.Aq = shift_of(Mq, ec);
@@ -635,22 +916,30 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     dc.rho_hi = 0.0f;
     dc.rho_lo = 0.0f;
   }
+  __shared__ DrawShared ds;
+  uint32_t fbad = sh.bad;
+  double total = 0.0;
+  int64_t token = -1;
 
-  // ---- tile sums of this workgroup's share of the tiles.  A tile is 2048
-  // logits: 256 consecutive groups, lane l holding groups l, l+64, l+128,
-  // l+192 (each 16-byte load instruction covers 1 KB of contiguous logits).
-  const int64_t per = (num_tiles + G - 1) / G;
-  const int64_t t_lo = (int64_t)g * per;
-  const int64_t t_hi = t_lo + per < num_tiles ? t_lo + per : num_tiles;
-  double* ts_seq = tile_sums + b * num_tiles;
-  {
+  if (!tile_pass) {
+    if (g != 0) return;                  // one workgroup draws from the task sums
+    token = draw_from_task_sums<DT, VEC>(part + (prow_t0 + n) * tpr, tpr, prow, V, dc, ec,
+                                         u_final, tile_sum, ds, fbad, total);
+  } else {
+    // ---- tile sums of this workgroup's share of the tiles.  A tile is 2048
+    // logits: 256 consecutive groups, lane l holding groups l, l+64, l+128,
+    // l+192 (each 16-byte load instruction covers 1 KB of contiguous logits).
+    const int64_t per = (num_tiles + G - 1) / G;
+    const int64_t t_lo = (int64_t)g * per;
+    const int64_t t_hi = t_lo + per < num_tiles ? t_lo + per : num_tiles;
+    double* ts_seq = tile_sums + b * num_tiles;
     for (int64_t t = t_lo + wave; t < t_hi; t += kWaves) {
       GroupRaw<DT> cp[kTileGroupsPerLane], cq[kTileGroupsPerLane];
 #pragma unroll
       for (int j = 0; j < kTileGroupsPerLane; ++j) {
         const int64_t gi = t * kTileGroups + j * 64 + lane;   // past V: all -inf
         load_group<DT, VEC>(prow, gi, V, cp[j]);
-        if (read_q) load_group<DT, VEC>(qrow, gi, V, cq[j]);
+        load_group<DT, VEC>(qrow, gi, V, cq[j]);
       }
       float lsum = 0.0f;
 #pragma unroll
@@ -665,135 +954,66 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
         else __hip_atomic_store(&ts_seq[t], ts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-  }
-  // ---- arrival: with G > 1 the tile sums cross workgroups.  They were
-  // written with agent-scope atomic stores (through to the device-coherent
-  // level); each wave waits for their acknowledgement before the barrier,
-  // then one thread counts the workgroup in.  The last of the G workgroups
-  // reads them back with agent-scope atomic loads.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (G > 1) {
-    __shared__ int last;
-    if (tid == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(&counters[b], 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-      last = (old == (uint32_t)(G - 1)) ? 1 : 0;
+    // ---- arrival: with G > 1 the tile sums cross workgroups.  They were
+    // written with agent-scope atomic stores (through to the device-coherent
+    // level); each wave waits for their acknowledgement before the barrier,
+    // then one thread counts the workgroup in.  The last of the G workgroups
+    // reads them back with agent-scope atomic loads.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (G > 1) {
+      if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&counters[b], 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        ds.last_wg = (old == (uint32_t)(G - 1)) ? 1 : 0;
+      }
+      __syncthreads();
+      if (!ds.last_wg) return;
+      // the last workgroup copies the tile sums into its LDS
+      for (int64_t t = tid; t < num_tiles; t += kThreads)
+        tile_sum[t] = __hip_atomic_load(&ts_seq[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+    }
+    // ---- wave 0 scans the tile sums in order and finds the tile holding
+    // t = u * S; an empty residual (invalid input or extreme rounding) falls
+    // back to a draw from p_n through the task sums.
+    if (wave == 0) {
+      double tt = 0.0;
+      total = wave_total(tile_sum, num_tiles, lane);
+      if (total > 0.0) {
+        tt = (double)u_final * total;
+        find_interval(tile_sum, num_tiles, tt, lane, ds);
+      }
+      if (lane == 0) {
+        ds.total = total;
+        ds.tt = tt;
+      }
     }
     __syncthreads();
-    if (!last) return;
-  }
-  if (wave != 0) return;
-
-  // ---- one wave finishes: scan the tile sums in order, find the tile
-  // holding t = u * S, re-scan it, take the smallest k with C_k > t.
-  auto tile_at = [&](int64_t t) -> double {
-    return G == 1 ? tile_sum[t]
-                  : __hip_atomic_load(&ts_seq[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  double total = 0.0;
-  for (int64_t c = 0; c < num_tiles; c += 64) {
-    const double v = (c + lane < num_tiles) ? tile_at(c + lane) : 0.0;
-    total += __shfl(wave_incl_scan(v, lane), 63);
-  }
-  uint32_t fbad = sh.bad;
-  DrawConsts dd = dc;
-  bool fallback = false;
-  if (!(total > 0.0)) {
-    // empty residual (invalid input or extreme rounding): draw from p_n;
-    // this wave recomputes every tile sum of the target row alone
-    fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
-    dd.residual = kDrawBonus;
-    fallback = true;
-    total = 0.0;
-    for (int64_t t = 0; t < num_tiles; ++t) {
-      float lsum = 0.0f;
-      for (int j = 0; j < kTileGroupsPerLane; ++j) {
-        GroupRaw<DT> r;
-        const int64_t gi = t * kTileGroups + j * 64 + lane;
-        load_group<DT, VEC>(prow, gi, V, r);
-        float w[kGroup];
-        weights_of<DT>(r, r, gi * kGroup, dd, ec, w);
-        lsum += seq_sum8(w);
+    total = ds.total;
+    if (!(total > 0.0)) {
+      fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
+      DrawConsts dd = dc;
+      dd.residual = kDrawBonus;
+      __syncthreads();   // ds is reused
+      double ptotal = 0.0;
+      token = draw_from_task_sums<DT, VEC>(part + (prow_t0 + n) * tpr, tpr, prow, V, dd, ec,
+                                           u_final, tile_sum, ds, fbad, ptotal);
+    } else {
+      // ---- re-scan tile tau: thread t < 256 holds group tau*256 + t
+      const int64_t tau = ds.tau;
+      GroupRaw<DT> rp, rq;
+      const bool active = tid < kTileGroups;
+      const int64_t gi = tau * kTileGroups + tid;
+      if (active) {
+        load_group<DT, VEC>(prow, gi, V, rp);
+        load_group<DT, VEC>(qrow, gi, V, rq);
       }
-      const double ts = wave_xor_sum((double)lsum);
-      if (lane == 0) tile_sum[t] = ts;   // LDS holds num_tiles doubles
-      total += ts;
+      token = block_search<DT>(rp, rq, gi, active, dc, ec, ds.tt, ds.p_excl, ds);
     }
   }
-  auto tile_final = [&](int64_t t) -> double { return fallback ? tile_sum[t] : tile_at(t); };
-  const double tt = (double)u_final * total;
-  double base = 0.0, P_excl = 0.0;
-  int64_t tau = -1;
-  for (int64_t c = 0; c < num_tiles && tau < 0; c += 64) {
-    const double v = (c + lane < num_tiles) ? tile_final(c + lane) : 0.0;
-    const double incl = base + wave_incl_scan(v, lane);
-    const uint64_t hit = __ballot(c + lane < num_tiles && incl > tt);
-    const double below = __shfl_up(incl, 1);
-    if (hit) {
-      const int l = __builtin_ctzll(hit);
-      tau = c + l;
-      P_excl = __shfl(lane == 0 ? base : below, l);
-    }
-    base = __shfl(incl, 63);
-  }
-  int64_t token = -1;
-  if (tau >= 0) {
-    // re-scan tile tau in ascending logit order: group j*64 + lane for
-    // j = 0..3, each a 64-lane scan on top of the previous groups' total
-    GroupRaw<DT> rp[kTileGroupsPerLane], rq[kTileGroupsPerLane];
-#pragma unroll
-    for (int j = 0; j < kTileGroupsPerLane; ++j) {
-      const int64_t gi = tau * kTileGroups + j * 64 + lane;
-      load_group<DT, VEC>(prow, gi, V, rp[j]);
-      if (MODE == kDraftLogits && dd.residual == kDrawResidual)
-        load_group<DT, VEC>(qrow, gi, V, rq[j]);
-    }
-    // the four 64-lane scans are independent; their totals chain in order.
-    // The weights are recomputed for the search (same code, same values)
-    // rather than held, to keep register pressure down.
-    double incl[kTileGroupsPerLane];
-#pragma unroll
-    for (int j = 0; j < kTileGroupsPerLane; ++j) {
-      float w[kGroup];
-      weights_of<DT>(rp[j], rq[j], (tau * kTileGroups + j * 64 + lane) * kGroup, dd, ec, w);
-      incl[j] = wave_incl_scan((double)seq_sum8(w), lane);
-    }
-    double run = P_excl;
-    int64_t last_pos = -1;
-#pragma unroll
-    for (int j = 0; j < kTileGroupsPerLane; ++j) {
-      const int64_t gi = tau * kTileGroups + j * 64 + lane;
-      float w[kGroup];
-      weights_of<DT>(rp[j], rq[j], gi * kGroup, dd, ec, w);
-      const double below = __shfl_up(incl[j], 1);
-      const double excl = lane == 0 ? 0.0 : below;
-      int k_hit = -1;
-      float c = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kGroup; ++k) {
-        c += w[k];
-        if (k_hit < 0 && w[k] > 0.0f && run + (excl + (double)c) > tt) k_hit = k;
-        if (w[k] > 0.0f) last_pos = gi * kGroup + k;
-      }
-      const uint64_t hit = __ballot(k_hit >= 0);
-      if (token < 0 && hit) {
-        const int l = __builtin_ctzll(hit);
-        token = (tau * kTileGroups + j * 64 + l) * kGroup + __shfl(k_hit, l);
-      }
-      run += __shfl(incl[j], 63);
-    }
-    if (token < 0) {   // rounding left t past the tile's last weight
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const int64_t ol = __shfl_xor(last_pos, o);
-        last_pos = ol > last_pos ? ol : last_pos;
-      }
-      token = last_pos;
-    }
-  }
-  if (lane == 0) {
+  if (tid == 0) {
     out_tokens[trow0 + n] = (int32_t)token;
     if (out_residual)
       out_residual[b] = (residual && !(fbad & SPEC_VERIFY_DEV_EMPTY_RESIDUAL))
