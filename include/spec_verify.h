@@ -143,9 +143,11 @@ typedef struct {
   uint32_t *status;            /* optional device word; the kernels OR
                                   SPEC_VERIFY_DEV_* bits into it (the caller
                                   clears it) */
-  void *const *timing_events;  /* optional: hipEvent_t[2 * kernels] recorded
-                                  on the stream before and after each kernel,
-                                  in launch order (see spec_verify_num_kernels) */
+  void *const *timing_events;  /* optional: hipEvent_t[2 * kernels], created
+                                  with timing enabled; events 2k and 2k+1 are
+                                  the start and stop events of kernel k's own
+                                  dispatch (hipExtLaunchKernel), in launch
+                                  order (see spec_verify_num_kernels) */
 } spec_verify_args;
 
 /*

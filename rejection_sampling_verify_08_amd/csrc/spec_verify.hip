@@ -3,6 +3,7 @@
 // on the caller's HIP stream.  The device code is in spec_verify_kernels.hpp
 // (sampled verification, with draft logits or point-mass drafts) and
 // greedy_kernels.hpp (greedy verification).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -97,6 +98,20 @@ int combine_lanes(int64_t tasks_per_row) {
 
 enum class Mode { kSampled, kPointDrafts, kGreedy };
 
+// Launch `kernel`; with timing events, the pair (ev[2k], ev[2k+1]) is the
+// dispatch's own start / stop event (no separate event packets on the
+// stream, so the recorded interval is the kernel's execution).
+template <typename F, typename... Args>
+hipError_t launch(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                  hipEvent_t const* ev, int k, Args... args) {
+  if (ev)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, ev[2 * k], ev[2 * k + 1], 0,
+                          args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+  return hipGetLastError();
+}
+
 template <int DT, bool VEC, bool CHECK, int MODE>
 hipError_t launch_sampled(const spec_verify_ctx* ctx, const spec_verify_args* a,
                           hipStream_t stream) {
@@ -117,13 +132,10 @@ hipError_t launch_sampled(const spec_verify_ctx* ctx, const spec_verify_args* a,
 
   // kernel 1: one pass over all target (and draft) rows
   const int64_t grid1 = ceil_div(rows * ctx->tasks_per_row, kStatsWaves);
-  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((row_stats_kernel<DT, VEC, CHECK>), dim3((unsigned)grid1),
-                     dim3(kStatsThreads), 0, stream, a->target_logits, draft, R_t,
-                     rows, a->ld, ctx->vocab, ctx->tasks_per_row, ec, partials, counters, B,
-                     a->status);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
+  e = launch(row_stats_kernel<DT, VEC, CHECK>, dim3((unsigned)grid1), dim3(kStatsThreads), 0,
+             stream, ev, 0, a->target_logits, draft, R_t, rows, a->ld, ctx->vocab,
+             ctx->tasks_per_row, ec, partials, counters, (int64_t)B, a->status);
+  if (e != hipSuccess) return e;
 
   // kernel 2: G workgroups per sequence, about one per compute unit in all,
   // sharing a residual's second pass over its rows.  Point-mass drafts never
@@ -131,17 +143,13 @@ hipError_t launch_sampled(const spec_verify_ctx* ctx, const spec_verify_args* a,
   int64_t G = ctx->cu_count / B;
   if (G > ctx->num_tiles) G = ctx->num_tiles;
   if (G < 1 || MODE == kDraftPoint) G = 1;
-  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   const size_t lds = (size_t)ctx->num_tiles * sizeof(double);
-  hipLaunchKernelGGL((finish_kernel<DT, VEC, CHECK, MODE>), dim3((unsigned)(B * G)),
-                     dim3(kThreads), lds, stream, a->target_logits, draft, a->ld, ctx->vocab, R_t,
-                     R_d, a->cu_draft, a->draft_tokens, a->uniforms, ec, partials,
-                     ctx->tasks_per_row, combine_lanes(ctx->tasks_per_row), ctx->num_tiles,
-                     (int)G, tiles, counters, a->out_tokens, a->out_num_accepted,
-                     a->out_p_draft, a->out_q_draft, a->out_residual_sum, a->status);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
-  return hipSuccess;
+  return launch(finish_kernel<DT, VEC, CHECK, MODE>, dim3((unsigned)(B * G)), dim3(kThreads), lds,
+                stream, ev, 1, a->target_logits, draft, a->ld, ctx->vocab, R_t, R_d,
+                a->cu_draft, a->draft_tokens, a->uniforms, ec, (const Partial*)partials,
+                ctx->tasks_per_row, combine_lanes(ctx->tasks_per_row), ctx->num_tiles, (int)G,
+                tiles, counters, a->out_tokens, a->out_num_accepted, a->out_p_draft,
+                a->out_q_draft, a->out_residual_sum, a->status);
 }
 
 template <int DT, bool VEC, bool CHECK>
@@ -157,20 +165,14 @@ hipError_t launch_greedy(const spec_verify_ctx* ctx, const spec_verify_args* a,
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(a->timing_events);
   hipError_t e;
   const int64_t grid1 = ceil_div(R_t * ctx->tasks_per_row, kStatsWaves);
-  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((argmax_kernel<DT, VEC, CHECK>), dim3((unsigned)grid1), dim3(kStatsThreads),
-                     0, stream, a->target_logits, R_t, a->ld, ctx->vocab, ctx->tasks_per_row,
-                     partials, a->status);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((greedy_finish_kernel<CHECK>), dim3((unsigned)B), dim3(kGreedyThreads), 0,
-                     stream, ctx->vocab, R_t, R_d, a->cu_draft, a->draft_tokens, partials,
-                     ctx->tasks_per_row, combine_lanes(ctx->tasks_per_row), a->out_tokens,
-                     a->out_num_accepted, a->status);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
-  return hipSuccess;
+  e = launch(argmax_kernel<DT, VEC, CHECK>, dim3((unsigned)grid1), dim3(kStatsThreads), 0, stream,
+             ev, 0, a->target_logits, R_t, a->ld, ctx->vocab, ctx->tasks_per_row, partials,
+             a->status);
+  if (e != hipSuccess) return e;
+  return launch(greedy_finish_kernel<CHECK>, dim3((unsigned)B), dim3(kGreedyThreads), 0, stream,
+                ev, 1, ctx->vocab, R_t, R_d, a->cu_draft, a->draft_tokens,
+                (const ArgPartial*)partials, ctx->tasks_per_row,
+                combine_lanes(ctx->tasks_per_row), a->out_tokens, a->out_num_accepted, a->status);
 }
 
 template <int DT, bool VEC, bool CHECK>
