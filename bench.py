@@ -258,6 +258,37 @@ def main() -> int:
                              "algorithmic_bytes_per_launch": m_first},
             }
 
+    # the adaptive draft-length controller after each verify call: one
+    # update of B controllers (window 50) from the call's accepted counts,
+    # enqueued on the same stream; latency-bound (one workgroup)
+    adapt = None
+    if not a.skip_modes:
+        from rejection_sampling_verify_08_amd import DraftLengthController, adapt_params
+        sampled_step(0, None)          # outs[0] holds a sampled call's counts again
+        ctl = DraftLengthController(inp.num_seqs, adapt_params("window50"), device=dev)
+        next_k = torch.empty(inp.num_seqs, dtype=torch.int32, device=dev)
+        next_cu = torch.empty(inp.num_seqs + 1, dtype=torch.int32, device=dev)
+        for _ in range(20):
+            ctl.update(cu, outs[0].num_accepted, next_k=next_k, next_cu=next_cu, stream=stream)
+        e0, e1 = make_events(2)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        n_upd = 200
+        for _ in range(n_upd):
+            ctl.update(cu, outs[0].num_accepted, next_k=next_k, next_cu=next_cu, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dev_us = e0.elapsed_time(e1) * 1e3 / n_upd
+        hctl = DraftLengthController(inp.num_seqs, adapt_params("window50"), device="host")
+        hcu, hacc = inp.cu_draft, outs[0].num_accepted.cpu().numpy()
+        t0 = time.perf_counter()
+        for _ in range(n_upd):
+            hctl.update(hcu, hacc)
+        host_us = (time.perf_counter() - t0) * 1e6 / n_upd
+        adapt = {"sequences": inp.num_seqs, "window": 50,
+                 "device_us_per_update": round(dev_us, 2), "host_us_per_update": round(host_us, 2),
+                 "bound": "latency", "accept_rate": round(ctl.accept_rate(), 4)}
+
     cpu = None
     if a.cpu_budget > 0:
         cpu = cpu_baseline(inp, a.cpu_budget)
@@ -277,6 +308,7 @@ def main() -> int:
         "mean_accepted": round(float(num_acc.mean()), 4), "status": status,
         "roofline": roof, "cpu_baseline": cpu,
         "modes": modes or None,
+        "adaptive_draft_length": adapt,
         "kernel_source_hash": src_hash,
     }
     print(json.dumps(line, ensure_ascii=False), flush=True)

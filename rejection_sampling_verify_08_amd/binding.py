@@ -32,7 +32,14 @@ EXPORTED = ("spec_verify_create", "spec_verify_query_workspace",
             "spec_verify_num_kernels", "spec_verify_run",
             "spec_verify_run_greedy", "spec_verify_run_point_drafts",
             "spec_verify_destroy", "spec_verify_status_string",
-            "spec_verify_last_hip_error")
+            "spec_verify_last_hip_error",
+            "spec_verify_adapt_preset", "spec_verify_adapt_state_bytes",
+            "spec_verify_adapt_reset", "spec_verify_adapt_update")
+
+# keep in step with include/spec_verify_adapt.h
+ADAPT_HOST = -1
+ADAPT_PRESETS = {"window50": 0, "last10": 1}
+ADAPT_BAD_SLOT, ADAPT_BAD_COUNTS = 1, 2
 
 
 class SpecVerifyError(RuntimeError):
@@ -71,6 +78,20 @@ class Args(ctypes.Structure):
     ]
 
 
+class AdaptParams(ctypes.Structure):
+    """spec_verify_adapt_params, field for field."""
+    _fields_ = [
+        ("k_min", ctypes.c_int32),
+        ("k_max", ctypes.c_int32),
+        ("k_init", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("min_history", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("up", ctypes.c_double),
+        ("down", ctypes.c_double),
+    ]
+
+
 _lib = None
 
 
@@ -101,6 +122,19 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P, ctypes.POINTER(Args), P]
+    AP = ctypes.POINTER(AdaptParams)
+    lib.spec_verify_adapt_preset.restype = ctypes.c_int
+    lib.spec_verify_adapt_preset.argtypes = [ctypes.c_int, AP]
+    lib.spec_verify_adapt_state_bytes.restype = ctypes.c_int
+    lib.spec_verify_adapt_state_bytes.argtypes = [AP, ctypes.c_int64,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+    lib.spec_verify_adapt_reset.restype = ctypes.c_int
+    lib.spec_verify_adapt_reset.argtypes = [AP, ctypes.c_int64, P, ctypes.c_size_t,
+                                            ctypes.c_int64, P, ctypes.c_int, P]
+    lib.spec_verify_adapt_update.restype = ctypes.c_int
+    lib.spec_verify_adapt_update.argtypes = [AP, ctypes.c_int64, P, ctypes.c_size_t,
+                                             ctypes.c_int32, P, P, P, P, P, P, P,
+                                             ctypes.c_int, P]
     lib.spec_verify_destroy.restype = ctypes.c_int
     lib.spec_verify_destroy.argtypes = [P]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
@@ -281,3 +315,111 @@ def verify(cu_draft, target_logits, draft_logits, draft_tokens, uniforms,
     sv = SpecVerifier(V, target_logits.dtype, max_seqs=max(B, 1),
                       max_draft_rows=R_d, device=target_logits.device, check=check)
     return sv(cu_draft, target_logits, draft_logits, draft_tokens, uniforms, temperature)
+
+
+def adapt_params(preset: str = "window50", **overrides) -> AdaptParams:
+    """A preset of spec_verify_adapt_preset, with fields overridden."""
+    lib = load_library()
+    p = AdaptParams()
+    st = lib.spec_verify_adapt_preset(ADAPT_PRESETS[preset], ctypes.byref(p))
+    if st != OK:
+        raise SpecVerifyError("spec_verify_adapt_preset", st)
+    for k, v in overrides.items():
+        setattr(p, k, v)
+    return p
+
+
+class DraftLengthController:
+    """Adaptive draft lengths for `num_slots` request slots plus acceptance
+    statistics (include/spec_verify_adapt.h).
+
+    device "host": state and arrays are numpy (the library computes on the
+    calling thread); otherwise a torch device: state and arrays are device
+    tensors and every call is enqueued on the stream.  Marshalling only."""
+
+    def __init__(self, num_slots: int, params: Optional[AdaptParams] = None,
+                 device="host"):
+        import numpy as np
+        self._np = np
+        self.lib = load_library()
+        self.params = params if params is not None else adapt_params()
+        self.num_slots = int(num_slots)
+        nbytes = ctypes.c_size_t()
+        st = self.lib.spec_verify_adapt_state_bytes(ctypes.byref(self.params), self.num_slots,
+                                                    ctypes.byref(nbytes))
+        if st != OK:
+            raise SpecVerifyError("spec_verify_adapt_state_bytes", st)
+        self.state_bytes = int(nbytes.value)
+        self.host = device == "host"
+        if self.host:
+            raw = np.zeros(self.state_bytes + 256, dtype=np.uint8)
+            off = (-raw.ctypes.data) % 256
+            self._raw = raw
+            self.state = raw[off:off + self.state_bytes]
+            self.stats = np.zeros(4, dtype=np.uint64)
+            self.status = np.zeros(1, dtype=np.uint32)
+            self.device_index = ADAPT_HOST
+        else:
+            import torch
+            self._torch = torch
+            dev = torch.device(device)
+            self.state = torch.zeros(max(self.state_bytes, 256), dtype=torch.uint8, device=dev)
+            self.stats = torch.zeros(4, dtype=torch.int64, device=dev)
+            self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+            self.device_index = dev.index or 0
+        self.reset()
+
+    def _p(self, a):
+        if a is None:
+            return None
+        return a.ctypes.data if self.host else int(a.data_ptr())
+
+    def _stream(self, stream):
+        if self.host:
+            return None
+        torch = self._torch
+        if stream is None:
+            stream = torch.cuda.current_stream(self.state.device)
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream")
+                               else int(stream))
+
+    def reset(self, slots=None, stream=None):
+        """Reset slots (all when None) to k_init with an empty history."""
+        n = self.num_slots if slots is None else int(slots.shape[0])
+        st = self.lib.spec_verify_adapt_reset(
+            ctypes.byref(self.params), self.num_slots, self._p(self.state), self.state_bytes, n,
+            self._p(slots), self.device_index, self._stream(stream))
+        if st != OK:
+            raise SpecVerifyError("spec_verify_adapt_reset", st, self.lib.spec_verify_last_hip_error())
+
+    def update(self, cu_draft, num_accepted, slots=None, next_k=None, next_cu=None,
+               stream=None):
+        """One step: returns (next_k [B], next_cu [B+1]) for the batch."""
+        B = int(cu_draft.shape[0]) - 1
+        if self.host:
+            np = self._np
+            next_k = np.empty(B, np.int32) if next_k is None else next_k
+            next_cu = np.empty(B + 1, np.int32) if next_cu is None else next_cu
+        else:
+            torch = self._torch
+            dev = self.state.device
+            next_k = torch.empty(B, dtype=torch.int32, device=dev) if next_k is None else next_k
+            next_cu = torch.empty(B + 1, dtype=torch.int32, device=dev) if next_cu is None else next_cu
+        st = self.lib.spec_verify_adapt_update(
+            ctypes.byref(self.params), self.num_slots, self._p(self.state), self.state_bytes, B,
+            self._p(slots), self._p(cu_draft), self._p(num_accepted), self._p(next_k),
+            self._p(next_cu), self._p(self.stats), self._p(self.status), self.device_index,
+            self._stream(stream))
+        if st != OK:
+            raise SpecVerifyError("spec_verify_adapt_update", st,
+                                  self.lib.spec_verify_last_hip_error())
+        return next_k, next_cu
+
+    def totals(self):
+        """(sequences, accepted, drafted, emitted) so far (synchronises)."""
+        v = self.stats if self.host else self.stats.cpu().numpy()
+        return tuple(int(x) for x in v.astype("uint64"))
+
+    def accept_rate(self) -> float:
+        _, acc, drafted, _ = self.totals()
+        return acc / drafted if drafted else 0.0

@@ -12,8 +12,10 @@
 #include <new>
 
 #include "spec_verify.h"
+#include "spec_verify_adapt.h"
 #include "spec_verify_kernels.hpp"
 #include "greedy_kernels.hpp"
+#include "adaptive_k.hpp"
 
 namespace {
 
@@ -325,5 +327,169 @@ const char* spec_verify_status_string(int status) {
 }
 
 int spec_verify_last_hip_error(void) { return g_last_hip_error; }
+
+// ------------------------------------------------------------------ adaptive draft length
+
+}  // extern "C"
+
+namespace {
+
+bool adapt_params_ok(const spec_verify_adapt_params* p) {
+  return p && p->k_min >= 0 && p->k_max >= p->k_min && p->k_init >= p->k_min &&
+         p->k_init <= p->k_max && p->window >= 1 && p->window <= SPEC_VERIFY_ADAPT_MAX_WINDOW &&
+         p->min_history >= 1 && p->min_history <= p->window && p->reserved == 0 &&
+         std::isfinite(p->up) && std::isfinite(p->down) && p->down <= p->up;
+}
+
+sv::AdaptParams adapt_params(const spec_verify_adapt_params* p) {
+  sv::AdaptParams q;
+  q.k_min = p->k_min;
+  q.k_max = p->k_max;
+  q.k_init = p->k_init;
+  q.window = p->window;
+  q.min_history = p->min_history;
+  q.up = p->up;
+  q.down = p->down;
+  return q;
+}
+
+// Common checks; on success *on_device says where the pointers live.
+int adapt_check(const spec_verify_adapt_params* p, int64_t num_slots, const void* state,
+                size_t state_bytes, int device) {
+  if (!adapt_params_ok(p) || num_slots < 0 || !state) return SPEC_VERIFY_EINVAL;
+  if (reinterpret_cast<uintptr_t>(state) % 256 != 0) return SPEC_VERIFY_EINVAL;
+  if (state_bytes < sv::adapt_layout(num_slots, p->window).total) return SPEC_VERIFY_ECAPACITY;
+  if (device < SPEC_VERIFY_ADAPT_HOST) return SPEC_VERIFY_EINVAL;
+  if (device >= 0) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cur != device) return SPEC_VERIFY_EINVAL;
+  }
+  return SPEC_VERIFY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_adapt_preset(int which, spec_verify_adapt_params* out) {
+  if (!out) return SPEC_VERIFY_EINVAL;
+  spec_verify_adapt_params p;
+  std::memset(&p, 0, sizeof(p));
+  if (which == SPEC_VERIFY_ADAPT_PRESET_WINDOW50) {
+    const double target = 0.6;
+    p.k_min = 2;
+    p.k_max = 8;
+    p.k_init = 2;
+    p.window = 50;
+    p.min_history = 10;
+    p.up = target + 0.1;
+    p.down = target - 0.1;
+  } else if (which == SPEC_VERIFY_ADAPT_PRESET_LAST10) {
+    p.k_min = 1;
+    p.k_max = 8;
+    p.k_init = 4;
+    p.window = 10;
+    p.min_history = 10;
+    p.up = 0.8;
+    p.down = 0.5;
+  } else {
+    return SPEC_VERIFY_EINVAL;
+  }
+  *out = p;
+  return SPEC_VERIFY_OK;
+}
+
+int spec_verify_adapt_state_bytes(const spec_verify_adapt_params* params, int64_t num_slots,
+                                  size_t* bytes) {
+  if (!adapt_params_ok(params) || num_slots < 0 || !bytes) return SPEC_VERIFY_EINVAL;
+  *bytes = sv::adapt_layout(num_slots, params->window).total;
+  return SPEC_VERIFY_OK;
+}
+
+int spec_verify_adapt_reset(const spec_verify_adapt_params* params, int64_t num_slots,
+                            void* state, size_t state_bytes, int64_t count,
+                            const int32_t* slots, int device, void* hip_stream) {
+  int rc = adapt_check(params, num_slots, state, state_bytes, device);
+  if (rc != SPEC_VERIFY_OK) return rc;
+  if (!slots) count = num_slots;
+  if (count < 0) return SPEC_VERIFY_EINVAL;
+  if (count == 0) return SPEC_VERIFY_OK;
+  const sv::AdaptParams p = adapt_params(params);
+  const sv::AdaptState st = sv::adapt_state(state, num_slots, params->window);
+  if (device == SPEC_VERIFY_ADAPT_HOST) {
+    for (int64_t i = 0; i < count; ++i) {
+      const int64_t s = slots ? (int64_t)slots[i] : i;
+      if (s >= 0 && s < num_slots) sv::adapt_reset_slot(p, st, s);
+    }
+    return SPEC_VERIFY_OK;
+  }
+  const int64_t grid = ceil_div(count, sv::kAdaptThreads);
+  hipLaunchKernelGGL(sv::adapt_reset_kernel, dim3((unsigned)grid), dim3(sv::kAdaptThreads), 0,
+                     static_cast<hipStream_t>(hip_stream), p, st, count, slots);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SPEC_VERIFY_OK : hip_fail(e);
+}
+
+int spec_verify_adapt_update(const spec_verify_adapt_params* params, int64_t num_slots,
+                             void* state, size_t state_bytes, int32_t num_seqs,
+                             const int32_t* slots, const int32_t* cu_draft,
+                             const int32_t* num_accepted, int32_t* next_k, int32_t* next_cu,
+                             uint64_t* stats, uint32_t* status, int device, void* hip_stream) {
+  int rc = adapt_check(params, num_slots, state, state_bytes, device);
+  if (rc != SPEC_VERIFY_OK) return rc;
+  if (num_seqs < 0) return SPEC_VERIFY_EINVAL;
+  if (!slots && num_seqs > num_slots) return SPEC_VERIFY_EINVAL;
+  if (num_seqs == 0) {
+    if (next_cu && device == SPEC_VERIFY_ADAPT_HOST) next_cu[0] = 0;
+    if (next_cu && device >= 0) {
+      // one int32 zero, written by a kernel so the call stays capturable
+      hipLaunchKernelGGL(sv::adapt_update_kernel, dim3(1), dim3(sv::kAdaptThreads), 0,
+                         static_cast<hipStream_t>(hip_stream), adapt_params(params),
+                         sv::adapt_state(state, num_slots, params->window), (int64_t)0,
+                         slots, cu_draft, num_accepted, next_k, next_cu,
+                         (unsigned long long*)nullptr, status);
+      hipError_t e = hipGetLastError();
+      return e == hipSuccess ? SPEC_VERIFY_OK : hip_fail(e);
+    }
+    return SPEC_VERIFY_OK;
+  }
+  if (!cu_draft || !num_accepted || !next_k) return SPEC_VERIFY_EINVAL;
+  const sv::AdaptParams p = adapt_params(params);
+  const sv::AdaptState st = sv::adapt_state(state, num_slots, params->window);
+  if (device == SPEC_VERIFY_ADAPT_HOST) {
+    int64_t run = 0;
+    uint64_t v = 0, a = 0, d = 0;
+    uint32_t bad = 0;
+    for (int64_t b = 0; b < num_seqs; ++b) {
+      const sv::AdaptOne r = sv::adapt_one(p, st, b, slots, cu_draft, num_accepted);
+      next_k[b] = r.k;
+      bad |= r.bad;
+      if (next_cu) next_cu[b] = (int32_t)run;
+      run += r.k;
+      if (r.valid) {
+        v += 1;
+        a += (uint64_t)num_accepted[b];
+        d += (uint64_t)(cu_draft[b + 1] - cu_draft[b]);
+      }
+    }
+    if (next_cu) next_cu[num_seqs] = (int32_t)run;
+    if (stats) {
+      stats[0] += v;
+      stats[1] += a;
+      stats[2] += d;
+      stats[3] += a + v;
+    }
+    if (status) *status |= bad;
+    return SPEC_VERIFY_OK;
+  }
+  hipLaunchKernelGGL(sv::adapt_update_kernel, dim3(1), dim3(sv::kAdaptThreads), 0,
+                     static_cast<hipStream_t>(hip_stream), p, st, (int64_t)num_seqs, slots,
+                     cu_draft, num_accepted, next_k, next_cu,
+                     reinterpret_cast<unsigned long long*>(stats), status);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SPEC_VERIFY_OK : hip_fail(e);
+}
 
 }  // extern "C"

@@ -1,7 +1,8 @@
 """The C-ABI library without a GPU: it loads, exports exactly what
-include/spec_verify.h declares, its argument struct matches the binding's
-layout, and the host-side argument checks return before any HIP call."""
+include/*.h declares, its argument structs match the binding's layouts, and
+the host-side argument checks return before any HIP call."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -12,11 +13,11 @@ import rejection_sampling_verify_08_amd as R
 from rejection_sampling_verify_08_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"SPEC_VERIFY_API\s+[\w\s\*]+?\b(spec_verify_\w+)\s*\(", text)))
 
 
@@ -52,10 +53,29 @@ def test_args_struct_layout_matches_header(tmp_path):
     assert int(got["sizeof"]) == ctypes.sizeof(binding.Args)
 
 
+def test_adapt_params_layout_matches_header(tmp_path):
+    fields = [f for f, _ in binding.AdaptParams._fields_]
+    src = tmp_path / "layout2.c"
+    body = "\n".join(
+        f'  printf("{f} %zu\\n", offsetof(spec_verify_adapt_params, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "spec_verify_adapt.h"\n'
+                   'int main(void){\n' + body +
+                   '\n  printf("sizeof %zu\\n", sizeof(spec_verify_adapt_params));\n  return 0;\n}\n')
+    exe = tmp_path / "layout2"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), "-o", str(exe),
+                    str(src)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                 check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(binding.AdaptParams, f).offset, f
+    assert int(got["sizeof"]) == ctypes.sizeof(binding.AdaptParams)
+
+
 def test_header_compiles_as_c_and_cpp(tmp_path):
     for comp, ext in (("gcc", "c"), ("g++", "cpp")):
         src = tmp_path / f"h.{ext}"
-        src.write_text('#include "spec_verify.h"\nint main(void){return SPEC_VERIFY_OK;}\n')
+        src.write_text('#include "spec_verify.h"\n#include "spec_verify_adapt.h"\n'
+                       'int main(void){return SPEC_VERIFY_OK;}\n')
         subprocess.run([comp, "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
                         "-o", str(tmp_path / f"h_{ext}"), str(src)], check=True)
 
