@@ -60,6 +60,13 @@ def _load():
         lib.oracle_verify_onehot.argtypes = [
             ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, P, P,
             ctypes.c_float, ctypes.c_double, P, P, P, P, P, P, P]
+        lib.oracle_verify_tree_greedy.restype = ctypes.c_int
+        lib.oracle_verify_tree_greedy.argtypes = [ctypes.c_int32, P, P, P, P, ctypes.c_int64,
+                                                  ctypes.c_int64, ctypes.c_int, P, P, P]
+        lib.oracle_verify_tree_point.restype = ctypes.c_int
+        lib.oracle_verify_tree_point.argtypes = [
+            ctypes.c_int32, P, P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, P,
+            ctypes.c_float, ctypes.c_double, P, P, P, P, P]
         lib.oracle_overlap_mass.restype = ctypes.c_double
         lib.oracle_overlap_mass.argtypes = [P, P, ctypes.c_int, ctypes.c_int64,
                                             ctypes.c_float]
@@ -240,4 +247,60 @@ def verify_onehot(num_seqs: int, cu_draft, target_logits, draft_tokens, uniforms
         _ptr(res.tie_accept) if R_d else None, _ptr(res.tie_final), _ptr(res.flagged))
     if rc != 0:
         raise ValueError(f"oracle_verify_onehot returned {rc}")
+    return res
+
+
+@dataclasses.dataclass
+class TreeResult:
+    out_tokens: np.ndarray       # int32 [R]: accepted tokens, final token, then -1
+    out_path: np.ndarray         # int32 [R]: accepted nodes' local indices, then -1
+    num_accepted: np.ndarray     # int32 [B]: accepted depth
+    tie: np.ndarray              # float64 [B]: smallest distance of a decision to its threshold
+    flagged: np.ndarray          # int32 [B]: 1 accept tie, 2 final-draw tie, 4 empty residual
+
+
+def _tree_common(cu_nodes, parent, tokens, target_logits, vocab, dtype):
+    tgt = np.ascontiguousarray(target_logits)
+    code = _dtype_code(tgt, dtype)
+    ld = tgt.shape[1]
+    V = ld if vocab is None else int(vocab)
+    return (tgt, code, ld, V, np.ascontiguousarray(cu_nodes, dtype=np.int32),
+            np.ascontiguousarray(parent, dtype=np.int32),
+            np.ascontiguousarray(tokens, dtype=np.int32))
+
+
+def verify_tree_greedy(num_seqs: int, cu_nodes, parent, tokens, target_logits, *,
+                       vocab=None, dtype=None) -> TreeResult:
+    """Greedy tree verification (see oracle.c)."""
+    lib = _load()
+    tgt, code, ld, V, cu, par, tok = _tree_common(cu_nodes, parent, tokens, target_logits,
+                                                  vocab, dtype)
+    B, R = int(num_seqs), tgt.shape[0]
+    res = TreeResult(np.full(R, -7, np.int32), np.full(R, -7, np.int32),
+                     np.zeros(B, np.int32), np.full(B, np.inf), np.zeros(B, np.int32))
+    rc = lib.oracle_verify_tree_greedy(B, _ptr(cu), _ptr(par), _ptr(tok), _ptr(tgt), ld, V,
+                                       code, _ptr(res.out_tokens), _ptr(res.out_path),
+                                       _ptr(res.num_accepted))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_tree_greedy returned {rc}")
+    return res
+
+
+def verify_tree_point(num_seqs: int, cu_nodes, parent, tokens, target_logits, uniforms,
+                      temperature: float, *, vocab=None, dtype=None,
+                      tie_tol: float = TIE_TOL) -> TreeResult:
+    """Tree verification of point-mass candidates (see oracle.c)."""
+    lib = _load()
+    tgt, code, ld, V, cu, par, tok = _tree_common(cu_nodes, parent, tokens, target_logits,
+                                                  vocab, dtype)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    B, R = int(num_seqs), tgt.shape[0]
+    res = TreeResult(np.full(R, -7, np.int32), np.full(R, -7, np.int32),
+                     np.zeros(B, np.int32), np.full(B, np.inf), np.zeros(B, np.int32))
+    rc = lib.oracle_verify_tree_point(B, _ptr(cu), _ptr(par), _ptr(tok), _ptr(tgt), ld, V,
+                                      code, _ptr(u), float(temperature), float(tie_tol),
+                                      _ptr(res.out_tokens), _ptr(res.out_path),
+                                      _ptr(res.num_accepted), _ptr(res.tie), _ptr(res.flagged))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_tree_point returned {rc}")
     return res

@@ -448,3 +448,194 @@ int oracle_verify_onehot(int32_t num_seqs, const int32_t *cu_draft,
   free(Mp); free(sp); free(w); free(C);
   return ORACLE_OK;
 }
+
+/*
+ * Tree verification.  "大模型推理加速新范式" section 3.2 (Tree Attention): the
+ * draft proposes several candidates per position, forming a tree, and the
+ * target scores every node of the tree in one pass, so that at least one
+ * path is more likely to be accepted.  The page gives no acceptance rule for
+ * a tree; the readings taken here are the plainest ones the rest of the
+ * pages support:
+ *   greedy (T -> 0):   from the root, move to the lowest-index child whose
+ *                      token is the argmax of the current node's row ([B]
+ *                      流程编排: compare with the target's choice); stop when
+ *                      no child matches and emit that argmax.
+ *   point candidates:  candidates carry no distribution (top-k proposals),
+ *                      so each is a point mass.  The children of the current
+ *                      node are tried in index order; child c is accepted
+ *                      with probability p'(x_c), where p' is the current
+ *                      node's p with the tokens of already rejected siblings
+ *                      removed and renormalised (the residual of the point
+ *                      rule, applied after each rejection); a token already
+ *                      rejected has p' = 0.  After every child is rejected,
+ *                      or at a node without children, the final token is
+ *                      drawn from p' (p itself when nothing was rejected).
+ *                      Each token then has exactly probability p_k of being
+ *                      emitted at each depth.
+ * Layout, per sequence b with N_b >= 1 nodes at global rows
+ * g = cu_nodes[b] + n, n in [0, N_b): node 0 is the root (the last
+ * committed token); parent[g] is the local index of node n's parent
+ * (0 <= parent < n for n >= 1); tokens[g] its token (ignored for the root);
+ * target row g is the target's distribution of the token after node n;
+ * uniforms[g] is node n's accept test (n >= 1) and the root's slot holds the
+ * final draw.  Outputs at the sequence's N_b slots: out_tokens = the accepted
+ * nodes' tokens, then the final token, then -1; out_path = the accepted
+ * nodes' local indices, then -1; out_num_accepted = the accepted depth.
+ */
+static int tree_geometry_ok(int32_t num_seqs, const int32_t *cu, const int32_t *parent,
+                            const int32_t *tokens, int64_t vocab, int need_tokens) {
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t g0 = cu[b], N = (int64_t)cu[b + 1] - cu[b];
+    if (N < 1) return 0;
+    for (int64_t n = 1; n < N; ++n) {
+      const int32_t pn = parent[g0 + n];
+      if (pn < 0 || pn >= n) return 0;
+      if (need_tokens && (tokens[g0 + n] < 0 || tokens[g0 + n] >= vocab)) return 0;
+    }
+  }
+  return 1;
+}
+
+int oracle_verify_tree_greedy(int32_t num_seqs, const int32_t *cu_nodes, const int32_t *parent,
+                              const int32_t *tokens, const void *target_logits, int64_t ld,
+                              int64_t vocab, int dtype, int32_t *out_tokens, int32_t *out_path,
+                              int32_t *out_num_accepted) {
+  if (num_seqs < 0 || vocab <= 0 || ld < vocab || (dtype != 0 && dtype != 1))
+    return ORACLE_EINVAL;
+  if (num_seqs == 0) return ORACLE_OK;
+  if (!cu_nodes || !parent || !tokens || !target_logits || !out_tokens || !out_path ||
+      !out_num_accepted)
+    return ORACLE_EINVAL;
+  if (!tree_geometry_ok(num_seqs, cu_nodes, parent, tokens, vocab, 1)) return ORACLE_EINVAL;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t g0 = cu_nodes[b], N = (int64_t)cu_nodes[b + 1] - cu_nodes[b];
+    for (int64_t n = 0; n < N; ++n) {
+      out_tokens[g0 + n] = -1;
+      out_path[g0 + n] = -1;
+    }
+    int64_t cur = 0, depth = 0;
+    for (;;) {
+      const int64_t a = row_argmax(target_logits, dtype, g0 + cur, ld, vocab);
+      int64_t next = -1;
+      for (int64_t n = cur + 1; n < N; ++n)
+        if (parent[g0 + n] == cur && tokens[g0 + n] == a) { next = n; break; }
+      out_tokens[g0 + depth] = (int32_t)a;
+      if (next < 0) break;
+      out_path[g0 + depth] = (int32_t)next;
+      ++depth;
+      cur = next;
+    }
+    out_num_accepted[b] = (int32_t)depth;
+  }
+  return ORACLE_OK;
+}
+
+int oracle_verify_tree_point(int32_t num_seqs, const int32_t *cu_nodes, const int32_t *parent,
+                             const int32_t *tokens, const void *target_logits, int64_t ld,
+                             int64_t vocab, int dtype, const float *uniforms, float temperature,
+                             double tie_tol, int32_t *out_tokens, int32_t *out_path,
+                             int32_t *out_num_accepted, double *out_tie, int32_t *flagged) {
+  if (num_seqs < 0 || vocab <= 0 || ld < vocab || (dtype != 0 && dtype != 1) ||
+      !(temperature > 0.0f) || !isfinite(temperature))
+    return ORACLE_EINVAL;
+  if (num_seqs == 0) return ORACLE_OK;
+  if (!cu_nodes || !parent || !tokens || !target_logits || !uniforms || !out_tokens ||
+      !out_path || !out_num_accepted)
+    return ORACLE_EINVAL;
+  if (!tree_geometry_ok(num_seqs, cu_nodes, parent, tokens, vocab, 1)) return ORACLE_EINVAL;
+  const double T = (double)temperature;
+  double *p = malloc(sizeof(double) * (size_t)vocab);
+  double *C = malloc(sizeof(double) * (size_t)vocab);
+  unsigned char *removed = calloc((size_t)vocab, 1);
+  if (!p || !C || !removed) { free(p); free(C); free(removed); return ORACLE_ENOMEM; }
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t g0 = cu_nodes[b], N = (int64_t)cu_nodes[b + 1] - cu_nodes[b];
+    for (int64_t n = 0; n < N; ++n) {
+      out_tokens[g0 + n] = -1;
+      out_path[g0 + n] = -1;
+    }
+    int32_t flag = 0;
+    double tie = INFINITY;
+    int64_t cur = 0, depth = 0;
+    for (;;) {
+      /* the current node's p */
+      double M, s;
+      row_normaliser(target_logits, dtype, g0 + cur, ld, vocab, T, &M, &s);
+      for (int64_t k = 0; k < vocab; ++k)
+        p[k] = prob(target_logits, dtype, g0 + cur, ld, k, T, M, s);
+      /* its children in index order, each a point-mass candidate */
+      int any_removed = 0;
+      int64_t next = -1;
+      for (int64_t n = cur + 1; n < N && next < 0; ++n) {
+        if (parent[g0 + n] != cur) continue;
+        const int64_t x = tokens[g0 + n];
+        double r;
+        if (removed[x]) {
+          r = 0.0;                     /* already rejected: p'(x) = 0 */
+        } else if (!any_removed) {
+          r = p[x];                    /* nothing removed yet: p' = p */
+        } else {
+          double rest = 0.0;           /* mass of the tokens not removed */
+          for (int64_t k = 0; k < vocab; ++k)
+            if (!removed[k]) rest += p[k];
+          r = p[x] / rest;
+        }
+        const double u = (double)uniforms[g0 + n];
+        const double d = fabs(u - r);
+        if (d < tie) tie = d;
+        if (d < tie_tol) flag |= 1;
+        if (u < r) {
+          next = n;
+        } else {
+          removed[x] = 1;
+          any_removed = 1;
+        }
+      }
+      if (next >= 0) {
+        for (int64_t n = cur + 1; n < N; ++n)    /* the next level starts afresh */
+          if (parent[g0 + n] == cur) removed[tokens[g0 + n]] = 0;
+        out_tokens[g0 + depth] = tokens[g0 + next];
+        out_path[g0 + depth] = (int32_t)next;
+        ++depth;
+        cur = next;
+        continue;
+      }
+      /* final draw from p without the rejected tokens */
+      double S = 0.0;
+      for (int64_t k = 0; k < vocab; ++k) {
+        S += removed[k] ? 0.0 : p[k];
+        C[k] = S;
+      }
+      int fallback = 0;
+      if (!(S > 0.0)) {
+        flag |= 4;
+        fallback = 1;
+        S = 0.0;
+        for (int64_t k = 0; k < vocab; ++k) { S += p[k]; C[k] = S; }
+      }
+      const double u = (double)uniforms[g0];
+      const double t = u * S;
+      int64_t tok = -1;
+      for (int64_t k = 0; k < vocab; ++k)
+        if (C[k] > t) { tok = k; break; }
+      if (tok < 0)
+        for (int64_t k = vocab - 1; k >= 0; --k)
+          if ((fallback || !removed[k]) && p[k] > 0.0) { tok = k; break; }
+      if (tok >= 0) {
+        const double lo = tok > 0 ? C[tok - 1] : 0.0;
+        double df = fmin(t - lo, C[tok] - t) / S;
+        if (df < 0.0) df = 0.0;
+        if (df < tie) tie = df;
+        if (df < tie_tol) flag |= 2;
+      }
+      out_tokens[g0 + depth] = (int32_t)tok;
+      for (int64_t n = 1; n < N; ++n) removed[tokens[g0 + n]] = 0;
+      break;
+    }
+    out_num_accepted[b] = (int32_t)depth;
+    if (out_tie) out_tie[b] = tie;
+    if (flagged) flagged[b] = flag;
+  }
+  free(p); free(C); free(removed);
+  return ORACLE_OK;
+}

@@ -16,6 +16,7 @@ import pytest
 import oracle
 from tests import test_oracle_pins as pins
 from tests import test_oracle_pins_modes as mpins
+from tests import test_oracle_pins_tree as tpins
 
 MUTANTS = [
     ("accept test in the wrong direction",
@@ -72,6 +73,37 @@ MODE_MUTANTS = [
     ("point: final draw uses the stopping position's uniform", POINT,
      "const double u = (double)uniforms[trow0 + gamma];",
      "const double u = (double)uniforms[trow0 + j];"),
+]
+
+TGREEDY = "int oracle_verify_tree_greedy("
+TPOINT = "int oracle_verify_tree_point("
+
+TREE_MUTANTS = [
+    ("tree greedy: the last matching child", TGREEDY,
+     "if (parent[g0 + n] == cur && tokens[g0 + n] == a) { next = n; break; }",
+     "if (parent[g0 + n] == cur && tokens[g0 + n] == a) { next = n; }"),
+    ("tree greedy: children of the root at every level", TGREEDY,
+     "if (parent[g0 + n] == cur && tokens[g0 + n] == a)",
+     "if (parent[g0 + n] == 0 && tokens[g0 + n] == a)"),
+    ("tree point: no renormalisation after a rejection", TPOINT,
+     "r = p[x] / rest;", "r = p[x];"),
+    ("tree point: rejected tokens kept in the final draw", TPOINT,
+     "S += removed[k] ? 0.0 : p[k];", "S += p[k];"),
+    ("tree point: a repeated token tested again", TPOINT,
+     "r = 0.0;                     /* already rejected: p'(x) = 0 */",
+     "r = p[x];"),
+    ("tree point: final draw with the stopping node's uniform", TPOINT,
+     "const double u = (double)uniforms[g0];", "const double u = (double)uniforms[g0 + cur];"),
+    ("tree point: removals carried to the next level", TPOINT,
+     "if (parent[g0 + n] == cur) removed[tokens[g0 + n]] = 0;",
+     "if (parent[g0 + n] == cur && 0) removed[tokens[g0 + n]] = 0;"),
+]
+
+TREE_PINS = [
+    (tpins.test_tree_golden_cases, {}),
+    (tpins.test_chain_trees_reduce_to_chain_verifiers, dict(dtype="bf16")),
+    (tpins.test_greedy_path_follows_numpy_argmax, {}),
+    (tpins.test_point_tree_output_law, {}),
 ]
 
 MODE_PINS = [
@@ -157,3 +189,10 @@ def _expect_caught(monkeypatch, lib, pin_list, name):
 def test_mode_pins_catch_mutant(tmp_path, monkeypatch, name, scope, old, new):
     lib = _build_mutant(tmp_path, old, new, scope)
     _expect_caught(monkeypatch, lib, MODE_PINS, name)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,scope,old,new", TREE_MUTANTS, ids=[m[0] for m in TREE_MUTANTS])
+def test_tree_pins_catch_mutant(tmp_path, monkeypatch, name, scope, old, new):
+    lib = _build_mutant(tmp_path, old, new, scope)
+    _expect_caught(monkeypatch, lib, TREE_PINS, name)

@@ -289,6 +289,116 @@ def with_deterministic_drafts(inp: VerifyInputs, name: Optional[str] = None) -> 
                                draft_tokens=tokens)
 
 
+# ---------------------------------------------------------------- candidate trees
+
+@dataclasses.dataclass
+class TreeInputs:
+    """One batch of candidate trees in the packed layout.
+
+    Sequence b owns nodes g = cu_nodes[b] + n, n in [0, N_b); node 0 is the
+    root (the last committed token).  parent[g] is the parent's local index
+    (0 <= parent < n), tokens[g] the node's token (root: -1), target row g
+    the target's logits for the token after node n, uniforms[g] node n's
+    accept test (n >= 1) and, at the root, the final draw."""
+
+    name: str
+    vocab: int
+    dtype: str
+    temperature: float
+    cu_nodes: np.ndarray       # int32 [B+1]
+    parent: np.ndarray         # int32 [R]
+    tokens: np.ndarray         # int32 [R]
+    target_logits: np.ndarray  # [R, V]
+    uniforms: np.ndarray       # float32 [R]
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.cu_nodes.shape[0]) - 1
+
+    @property
+    def rows(self) -> int:
+        return int(self.target_logits.shape[0])
+
+
+def tree_shape(levels) -> np.ndarray:
+    """Local parent indices of a tree in breadth-first order.  levels is a
+    list of (parents, children): the first `parents` nodes of the previous
+    level each get `children` children.  [(1, 4), (2, 3), (2, 2), (1, 2)]
+    gives 1 + 4 + 6 + 4 + 2 = 17 nodes."""
+    parent = [-1]
+    prev = [0]
+    for n_par, n_ch in levels:
+        cur = []
+        for pnode in prev[:n_par]:
+            for _ in range(n_ch):
+                parent.append(pnode)
+                cur.append(len(parent) - 1)
+        prev = cur
+    return np.asarray(parent, dtype=np.int32)
+
+
+def build_tree(name: str, seed: int, shapes, vocab: int, dtype: str, temperature: float,
+               target_row: RowFn, draft_sd: float, workers: Optional[int] = None) -> TreeInputs:
+    """Candidate trees: sequence b has the local parent array shapes[b].  A
+    node's children carry the top tokens (largest first, distinct) of a draft
+    row made of the node's float64 target row plus N(0, draft_sd^2) noise --
+    a drafter proposing its top-k at each expanded node.  Seeding as in
+    build(): SeedSequence(seed).spawn(6), one child per row for the target,
+    boost and draft-noise streams."""
+    ss = np.random.SeedSequence(seed).spawn(6)
+    sizes = np.asarray([len(sh) for sh in shapes], dtype=np.int64)
+    cu = np.zeros(len(shapes) + 1, dtype=np.int64)
+    np.cumsum(sizes, out=cu[1:])
+    R = int(cu[-1])
+    store = np.float32 if dtype == F32 else np.uint16
+    tgt = np.empty((R, vocab), dtype=store)
+    parent = np.empty(R, dtype=np.int32)
+    tokens = np.full(R, -1, dtype=np.int32)
+    r_tgt = _child(ss[_S_TARGET], R)
+    r_boost = _child(ss[_S_BOOST], R)
+    r_draft = _child(ss[_S_DRAFT], R)
+
+    def one_seq(b: int) -> None:
+        sh = np.asarray(shapes[b], dtype=np.int32)
+        g0 = int(cu[b])
+        parent[g0:g0 + len(sh)] = sh
+        for n in range(len(sh)):
+            t64 = target_row(r_tgt[g0 + n], r_boost[g0 + n], vocab)
+            tgt[g0 + n] = to_dtype(t64, dtype)
+            kids = np.nonzero(sh == n)[0]
+            if kids.size:
+                d = t64 + r_draft[g0 + n].standard_normal(vocab) * draft_sd
+                top = np.argsort(-d, kind="stable")[:kids.size]
+                tokens[g0 + kids] = top.astype(np.int32)
+
+    n_work = workers or min(16, os.cpu_count() or 1)
+    if R * vocab < (1 << 18) or n_work <= 1:
+        for b in range(len(shapes)):
+            one_seq(b)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(n_work) as ex:
+            list(ex.map(one_seq, range(len(shapes))))
+    r_unif = np.random.Generator(np.random.PCG64(ss[_S_UNIF]))
+    return TreeInputs(name=name, vocab=vocab, dtype=dtype,
+                      temperature=float(np.float32(temperature)),
+                      cu_nodes=cu.astype(np.int32), parent=parent, tokens=tokens,
+                      target_logits=tgt, uniforms=uniform_grid24(r_unif, R))
+
+
+TREE_17 = [(1, 4), (2, 3), (2, 2), (1, 2)]   # 17 nodes, depth 4
+
+
+def tree_config(seed: int = 6, num_seqs: int = 128, vocab: int = 128256) -> TreeInputs:
+    """The named tree workload: 128 sequences with 17-node candidate trees
+    (top-4 at the root, top-3 under the two best, top-2 below; 2176 rows,
+    as many as the headline chain batch), V = 128256 bf16, T = 1.0,
+    heavy-tailed target rows and draft noise as in the headline workload."""
+    shape = tree_shape(TREE_17)
+    return build_tree(f"trees B={num_seqs} 17 nodes V={vocab} bf16 T=1.0", seed,
+                      [shape] * num_seqs, vocab, BF16, 1.0, boosted_top_rows(2.0, 50, 6.0),
+                      HEAVY_TAIL_DRAFT_SIGMA)
+
+
 # ---------------------------------------------------------------- named workloads
 
 def _gamma_stream(seed: int) -> np.random.Generator:
