@@ -35,7 +35,8 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "verified rows/s + achieved HBM GB/s (% peak), B=128 γ=8 V=128256 bf16"
 PMC_FILE = os.path.join(ROOT, "profiles", "verify_kernels_B128_g8_V128256_bf16.pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_08_amd", "csrc", f)
-                  for f in ("spec_verify_kernels.hpp", "greedy_kernels.hpp", "spec_verify.hip")]
+                  for f in ("spec_verify_kernels.hpp", "greedy_kernels.hpp", "tree_kernels.hpp",
+                           "spec_verify.hip")]
 
 
 def kernel_source_hash() -> str:
@@ -137,10 +138,13 @@ def main() -> int:
           flush=True)
     tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
 
-    def up(arr):
-        if inp.dtype == "bf16":
+    def torch_rows(arr, dtype):
+        if dtype == "bf16":
             return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(arr).to(dev)
+
+    def up(arr):
+        return torch_rows(arr, inp.dtype)
 
     host_t, host_d = up(inp.target_logits), up(inp.draft_logits)
     sets = []
@@ -257,6 +261,50 @@ def main() -> int:
                              "kernel": kname, "kernel_avg_us": round(m_k[0] * 1e3, 2),
                              "algorithmic_bytes_per_launch": m_first},
             }
+
+    # tree verification on the named tree workload (128 trees of 17 nodes,
+    # 2176 rows: as many as the chain batch above)
+    if not a.skip_modes and a.config == 3:
+        tr = W.tree_config()
+        t_tree = torch_rows(tr.target_logits, inp.dtype)
+        tsets = [t_tree] + [t_tree.clone() for _ in range(max(1, a.sets) - 1)]
+        dvc = lambda arr: torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+        tcu, tpar, ttok, tuni = dvc(tr.cu_nodes), dvc(tr.parent), dvc(tr.tokens), dvc(tr.uniforms)
+        tree_out = [None] * len(tsets)
+
+        def tree_step(kind):
+            def step(i, events):
+                j = i % len(tsets)
+                if kind == "tree_greedy":
+                    tree_out[j] = sv.tree_greedy(tcu, tpar, ttok, tsets[j], out=tree_out[j],
+                                                 timing_events=events, stream=stream)
+                else:
+                    tree_out[j] = sv.tree_point(tcu, tpar, ttok, tsets[j], tuni, tr.temperature,
+                                                out=tree_out[j], timing_events=events,
+                                                stream=stream)
+            return step
+
+        for kind, kname, fname in (("tree_greedy", "argmax_kernel", "tree_greedy_kernel"),
+                                   ("tree_point", "row_stats_kernel", "tree_point_kernel")):
+            m_ms, m_k = timed(tree_step(kind))
+            depth = tree_out[0].num_accepted.cpu().numpy()
+            m_first = tr.rows * tr.vocab * (2 if tr.dtype == "bf16" else 4)
+            m_ach = m_first / (m_k[0] / 1e3) / 1e9
+            modes[kind] = {
+                "workload": tr.name,
+                "value": round(tr.rows / (m_ms / 1e3), 1), "unit": "verified node rows/s",
+                "ms_per_step": round(m_ms, 5),
+                "kernel_avg_us": [round(x * 1e3, 2) for x in m_k],
+                "kernel_names": [kname, fname],
+                "mean_accepted_depth": round(float(depth.mean()), 4),
+                "status": int(tree_out[0].status.cpu().item()),
+                "roofline": {"bound": "hbm", "achieved": round(m_ach, 1), "peak": PEAK_HBM_GBPS,
+                             "unit": "GB/s", "frac": round(m_ach / PEAK_HBM_GBPS, 4),
+                             "traffic": traffic_from_profile(src_hash, kind),
+                             "kernel": kname, "kernel_avg_us": round(m_k[0] * 1e3, 2),
+                             "algorithmic_bytes_per_launch": m_first},
+            }
+        del tsets
 
     # the adaptive draft-length controller after each verify call: one
     # update of B controllers (window 50) from the call's accepted counts,

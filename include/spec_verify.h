@@ -115,6 +115,16 @@ extern "C" {
 #define SPEC_VERIFY_DEV_ZERO_Q 32u       /* (CHECK) q_i(x_i) = 0 */
 #define SPEC_VERIFY_DEV_EMPTY_RESIDUAL 64u /* the residual summed to 0; the draw
                                               fell back to p at that position */
+#define SPEC_VERIFY_DEV_BAD_TREE 128u    /* a tree with more than
+                                            SPEC_VERIFY_MAX_TREE_NODES nodes, a
+                                            parent not before its child, a token
+                                            outside [0, V) or more than
+                                            SPEC_VERIFY_MAX_TREE_CHILDREN children
+                                            of one node; the sequence is skipped */
+
+/* Tree limits (per sequence). */
+#define SPEC_VERIFY_MAX_TREE_NODES 1024
+#define SPEC_VERIFY_MAX_TREE_CHILDREN 64
 
 typedef struct spec_verify_ctx spec_verify_ctx;
 
@@ -237,6 +247,66 @@ SPEC_VERIFY_API int spec_verify_run_greedy(const spec_verify_ctx *ctx,
 SPEC_VERIFY_API int spec_verify_run_point_drafts(const spec_verify_ctx *ctx,
                                                  const spec_verify_args *args,
                                                  void *hip_stream);
+
+/*
+ * Tree verification.  [D] section 3.2 (Tree Attention): the drafter proposes
+ * its top candidates at each position, forming a tree, and the target scores
+ * every node of the tree in one pass.  The page gives no acceptance rule; the
+ * readings fixed here:
+ *   greedy (spec_verify_tree_run_greedy): from the root, move to the
+ *     lowest-index child whose token is the argmax of the current node's row
+ *     (lowest id among equal maxima; [B] 流程编排); where no child matches,
+ *     emit that argmax.
+ *   point-mass candidates (spec_verify_tree_run_point): candidates carry no
+ *     distribution, so each is a point mass ([A] 1.2 step 3 with q = delta_x).
+ *     The current node's children are tried in index order; child c is
+ *     accepted iff u_c < p'(x_c), p' being the node's p = softmax(l / T) with
+ *     the tokens of already rejected siblings removed and renormalised (a
+ *     token already rejected has p' = 0).  When every child is rejected, or
+ *     at a node without children, the final token is drawn from p' with the
+ *     root's uniform (inverse CDF as in spec_verify_run).  Each token is then
+ *     emitted with probability exactly p_k at every depth.
+ * Layout (packed, one launch for any mix of tree shapes): sequence b owns
+ * the nodes g = cu_nodes[b] + n, 0 <= n < N_b, N_b >= 1; node 0 is the root
+ * (the last committed token).  parent[g] is node n's parent as a local index
+ * with 0 <= parent < n (root: ignored); tokens[g] its token (root: ignored);
+ * target row g (pitch ld) the target's logits for the token after node n;
+ * uniforms[g] node n's accept test, the root's slot the final draw.
+ * Outputs at the sequence's N_b slots: out_tokens = the accepted nodes'
+ * tokens, then the final token, then -1; out_path = the accepted nodes'
+ * local indices (which KV entries to keep), then -1; out_num_accepted[b] =
+ * the accepted depth.  The context's workspace holds the row statistics of
+ * up to max_seqs + 2 * max_draft_rows nodes and at most max_seqs trees.
+ * Errors as spec_verify_run; a malformed tree is skipped (outputs -1, status
+ * SPEC_VERIFY_DEV_BAD_TREE).  Two kernels: a row pass over the R node rows
+ * and one workgroup per tree.
+ */
+typedef struct {
+  int32_t num_seqs;            /* B >= 0 (host scalar) */
+  int64_t total_nodes;         /* R = cu_nodes[B] (host scalar) */
+  const int32_t *cu_nodes;     /* [B+1] */
+  const int32_t *parent;       /* [R] */
+  const int32_t *tokens;       /* [R] */
+  const void *target_logits;   /* [R rows, pitch ld] of the context's dtype */
+  int64_t ld;                  /* >= V */
+  const float *uniforms;       /* [R]; point-mass candidates only */
+  float temperature;           /* T > 0; point-mass candidates only */
+  int32_t *out_tokens;         /* [R] */
+  int32_t *out_path;           /* [R] */
+  int32_t *out_num_accepted;   /* [B] */
+  void *workspace;             /* as in spec_verify_args */
+  size_t workspace_bytes;
+  uint32_t *status;            /* optional */
+  void *const *timing_events;  /* optional, as in spec_verify_args */
+} spec_verify_tree_args;
+
+SPEC_VERIFY_API int spec_verify_tree_run_greedy(const spec_verify_ctx *ctx,
+                                                const spec_verify_tree_args *args,
+                                                void *hip_stream);
+
+SPEC_VERIFY_API int spec_verify_tree_run_point(const spec_verify_ctx *ctx,
+                                               const spec_verify_tree_args *args,
+                                               void *hip_stream);
 
 /* Destroy a context (NULL is accepted).  Returns OK. */
 SPEC_VERIFY_API int spec_verify_destroy(spec_verify_ctx *ctx);

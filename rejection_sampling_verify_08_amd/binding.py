@@ -26,11 +26,14 @@ DEV_BAD_LOGIT = 8
 DEV_EMPTY_ROW = 16
 DEV_ZERO_Q = 32
 DEV_EMPTY_RESIDUAL = 64
+DEV_BAD_TREE = 128
+MAX_TREE_NODES, MAX_TREE_CHILDREN = 1024, 64
 
 EXPORTED = ("spec_verify_create", "spec_verify_query_workspace",
             "spec_verify_workspace_size",
             "spec_verify_num_kernels", "spec_verify_run",
             "spec_verify_run_greedy", "spec_verify_run_point_drafts",
+            "spec_verify_tree_run_greedy", "spec_verify_tree_run_point",
             "spec_verify_destroy", "spec_verify_status_string",
             "spec_verify_last_hip_error",
             "spec_verify_adapt_preset", "spec_verify_adapt_state_bytes",
@@ -71,6 +74,28 @@ class Args(ctypes.Structure):
         ("out_p_draft", ctypes.c_void_p),
         ("out_q_draft", ctypes.c_void_p),
         ("out_residual_sum", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("status", ctypes.c_void_p),
+        ("timing_events", ctypes.c_void_p),
+    ]
+
+
+class TreeArgs(ctypes.Structure):
+    """spec_verify_tree_args, field for field."""
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("total_nodes", ctypes.c_int64),
+        ("cu_nodes", ctypes.c_void_p),
+        ("parent", ctypes.c_void_p),
+        ("tokens", ctypes.c_void_p),
+        ("target_logits", ctypes.c_void_p),
+        ("ld", ctypes.c_int64),
+        ("uniforms", ctypes.c_void_p),
+        ("temperature", ctypes.c_float),
+        ("out_tokens", ctypes.c_void_p),
+        ("out_path", ctypes.c_void_p),
+        ("out_num_accepted", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("status", ctypes.c_void_p),
@@ -122,6 +147,10 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P, ctypes.POINTER(Args), P]
+    for name in ("spec_verify_tree_run_greedy", "spec_verify_tree_run_point"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P, ctypes.POINTER(TreeArgs), P]
     AP = ctypes.POINTER(AdaptParams)
     lib.spec_verify_adapt_preset.restype = ctypes.c_int
     lib.spec_verify_adapt_preset.argtypes = [ctypes.c_int, AP]
@@ -143,6 +172,14 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_last_hip_error.argtypes = []
     _lib = lib
     return lib
+
+
+@dataclasses.dataclass
+class TreeOutput:
+    out_tokens: "torch.Tensor"          # int32 [R]
+    out_path: "torch.Tensor"            # int32 [R]
+    num_accepted: "torch.Tensor"        # int32 [B]
+    status: Optional["torch.Tensor"]    # int32 [1]
 
 
 @dataclasses.dataclass
@@ -257,6 +294,57 @@ class SpecVerifier:
         return self._run("spec_verify_run_greedy", cu_draft, target_logits, None,
                          draft_tokens, None, 1.0, num_seqs, int(draft_tokens.numel()),
                          out, timing_events, stream)
+
+    def tree_greedy(self, cu_nodes, parent, tokens, target_logits, **kw) -> TreeOutput:
+        """Greedy tree verification (spec_verify_tree_run_greedy)."""
+        return self._run_tree("spec_verify_tree_run_greedy", cu_nodes, parent, tokens,
+                              target_logits, None, 1.0, **kw)
+
+    def tree_point(self, cu_nodes, parent, tokens, target_logits, uniforms, temperature: float,
+                   **kw) -> TreeOutput:
+        """Tree verification of point-mass candidates (spec_verify_tree_run_point)."""
+        return self._run_tree("spec_verify_tree_run_point", cu_nodes, parent, tokens,
+                              target_logits, uniforms, temperature, **kw)
+
+    def _run_tree(self, entry, cu_nodes, parent, tokens, target_logits, uniforms, temperature,
+                  out: Optional[TreeOutput] = None, timing_events=None, stream=None):
+        torch = self._torch
+        B = int(cu_nodes.shape[0]) - 1
+        R = int(target_logits.shape[0])
+        dev = self.device
+        if out is None:
+            out = TreeOutput(torch.empty(R, dtype=torch.int32, device=dev),
+                             torch.empty(R, dtype=torch.int32, device=dev),
+                             torch.empty(B, dtype=torch.int32, device=dev),
+                             torch.zeros(1, dtype=torch.int32, device=dev))
+        if target_logits.dtype != self.torch_dtype or target_logits.stride(-1) != 1:
+            raise ValueError(f"target_logits must be {self.torch_dtype} with unit column stride")
+        for name, t, dt in (("cu_nodes", cu_nodes, torch.int32), ("parent", parent, torch.int32),
+                            ("tokens", tokens, torch.int32), ("uniforms", uniforms, torch.float32)):
+            if t is not None and (t.dtype != dt or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous {dt} tensor")
+        events = None
+        if timing_events is not None:
+            events = (ctypes.c_void_p * len(timing_events))(
+                *[ctypes.c_void_p(int(e.cuda_event)) if hasattr(e, "cuda_event") else e
+                  for e in timing_events])
+        a = TreeArgs(num_seqs=B, total_nodes=R, cu_nodes=_ptr(cu_nodes), parent=_ptr(parent),
+                     tokens=_ptr(tokens), target_logits=_ptr(target_logits),
+                     ld=int(target_logits.stride(0)), uniforms=_ptr(uniforms),
+                     temperature=float(temperature), out_tokens=_ptr(out.out_tokens),
+                     out_path=_ptr(out.out_path), out_num_accepted=_ptr(out.num_accepted),
+                     workspace=_ptr(self.workspace), workspace_bytes=int(self.workspace.numel()),
+                     status=_ptr(out.status),
+                     timing_events=ctypes.cast(events, ctypes.c_void_p) if events is not None else None)
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        lib = load_library()
+        st = getattr(lib, entry)(self._ctx, ctypes.byref(a), ctypes.c_void_p(handle))
+        if st != OK:
+            raise SpecVerifyError(entry, st, lib.spec_verify_last_hip_error())
+        self._keepalive = events
+        return out
 
     def _run(self, entry, cu_draft, target_logits, draft_logits, draft_tokens, uniforms,
              temperature, num_seqs, total_draft_rows, out, timing_events, stream):

@@ -15,7 +15,11 @@
 #include "spec_verify_adapt.h"
 #include "spec_verify_kernels.hpp"
 #include "greedy_kernels.hpp"
+#include "tree_kernels.hpp"
 #include "adaptive_k.hpp"
+
+static_assert(sv::kMaxTreeNodes == SPEC_VERIFY_MAX_TREE_NODES, "tree node limit");
+static_assert(sv::kMaxChildren == SPEC_VERIFY_MAX_TREE_CHILDREN, "tree child limit");
 
 namespace {
 
@@ -242,9 +246,103 @@ int run_mode(const spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_st
   return SPEC_VERIFY_OK;
 }
 
+// ---- tree verification
+
+template <int DT, bool VEC, bool CHECK>
+hipError_t launch_tree(const spec_verify_ctx* ctx, const spec_verify_tree_args* a,
+                       hipStream_t stream, bool greedy) {
+  using namespace sv;
+  const int64_t B = a->num_seqs;
+  const int64_t R = a->total_nodes;
+  char* ws = static_cast<char*>(a->workspace);
+  hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(a->timing_events);
+  const int64_t grid1 = ceil_div(R * ctx->tasks_per_row, kStatsWaves);
+  const int L = combine_lanes(ctx->tasks_per_row);
+  hipError_t e;
+  if (greedy) {
+    ArgPartial* partials = reinterpret_cast<ArgPartial*>(ws + ctx->layout.partials);
+    e = launch(argmax_kernel<DT, VEC, CHECK>, dim3((unsigned)grid1), dim3(kStatsThreads), 0,
+               stream, ev, 0, a->target_logits, R, a->ld, ctx->vocab, ctx->tasks_per_row,
+               partials, a->status);
+    if (e != hipSuccess) return e;
+    return launch(tree_greedy_kernel, dim3((unsigned)B), dim3(kGreedyThreads), 0, stream, ev, 1,
+                  ctx->vocab, R, a->cu_nodes, a->parent, a->tokens, (const ArgPartial*)partials,
+                  ctx->tasks_per_row, L, a->out_tokens, a->out_path, a->out_num_accepted,
+                  a->status);
+  }
+  Partial* partials = reinterpret_cast<Partial*>(ws + ctx->layout.partials);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + ctx->layout.counters);
+  const ExpConsts ec = exp_consts(a->temperature);
+  e = launch(row_stats_kernel<DT, VEC, CHECK>, dim3((unsigned)grid1), dim3(kStatsThreads), 0,
+             stream, ev, 0, a->target_logits, (const void*)nullptr, R, R, a->ld, ctx->vocab,
+             ctx->tasks_per_row, ec, partials, counters, (int64_t)0, a->status);
+  if (e != hipSuccess) return e;
+  const size_t lds = 2 * (size_t)ctx->tasks_per_row * sizeof(double);
+  return launch(tree_point_kernel<DT, VEC>, dim3((unsigned)B), dim3(kThreads), lds, stream, ev, 1,
+                a->target_logits, a->ld, ctx->vocab, R, a->cu_nodes, a->parent, a->tokens,
+                a->uniforms, ec, (const Partial*)partials, ctx->tasks_per_row, L,
+                a->out_tokens, a->out_path, a->out_num_accepted, a->status);
+}
+
+template <int DT>
+hipError_t dispatch_tree(const spec_verify_ctx* ctx, const spec_verify_tree_args* a,
+                         hipStream_t s, bool vec, bool check, bool greedy) {
+  if (vec) return check ? launch_tree<DT, true, true>(ctx, a, s, greedy)
+                        : launch_tree<DT, true, false>(ctx, a, s, greedy);
+  return check ? launch_tree<DT, false, true>(ctx, a, s, greedy)
+               : launch_tree<DT, false, false>(ctx, a, s, greedy);
+}
+
+int run_tree(const spec_verify_ctx* ctx, const spec_verify_tree_args* a, void* hip_stream,
+             bool greedy) {
+  if (!ctx || !a) return SPEC_VERIFY_EINVAL;
+  const int64_t B = a->num_seqs;
+  const int64_t R = a->total_nodes;
+  if (B < 0 || R < 0) return SPEC_VERIFY_EINVAL;
+  if (!greedy && (!(a->temperature > 0.0f) || !std::isfinite(a->temperature)))
+    return SPEC_VERIFY_EINVAL;
+  if (a->ld < ctx->vocab) return SPEC_VERIFY_EINVAL;
+  if (B > ctx->max_seqs || R > (int64_t)ctx->max_seqs + 2 * ctx->max_draft_rows)
+    return SPEC_VERIFY_ECAPACITY;
+  if (B == 0) return SPEC_VERIFY_OK;
+  if (R < B) return SPEC_VERIFY_EINVAL;   // every tree has a root
+  const size_t esize = ctx->dtype == SPEC_VERIFY_BF16 ? 2 : 4;
+  if (!a->cu_nodes || !a->parent || !a->tokens || !a->target_logits || !a->out_tokens ||
+      !a->out_path || !a->out_num_accepted || !a->workspace)
+    return SPEC_VERIFY_EINVAL;
+  if (!greedy && !a->uniforms) return SPEC_VERIFY_EINVAL;
+  if (!aligned(a->target_logits, esize) || !aligned(a->cu_nodes, 4) || !aligned(a->parent, 4) ||
+      !aligned(a->tokens, 4) || (!greedy && !aligned(a->uniforms, 4)) ||
+      !aligned(a->out_tokens, 4) || !aligned(a->out_path, 4) ||
+      !aligned(a->out_num_accepted, 4) || !aligned(a->workspace, kAlign))
+    return SPEC_VERIFY_EINVAL;
+  if (a->workspace_bytes < ctx->layout.total) return SPEC_VERIFY_ECAPACITY;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e);
+  if (cur != ctx->device) return SPEC_VERIFY_EINVAL;
+  const bool vec = aligned(a->target_logits, 16) && ((size_t)a->ld * esize) % 16 == 0;
+  const bool check = (ctx->flags & SPEC_VERIFY_FLAG_CHECK) != 0;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  e = ctx->dtype == SPEC_VERIFY_BF16 ? dispatch_tree<1>(ctx, a, s, vec, check, greedy)
+                                     : dispatch_tree<0>(ctx, a, s, vec, check, greedy);
+  if (e != hipSuccess) return hip_fail(e);
+  return SPEC_VERIFY_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int spec_verify_tree_run_greedy(const spec_verify_ctx* ctx, const spec_verify_tree_args* a,
+                                void* hip_stream) {
+  return run_tree(ctx, a, hip_stream, true);
+}
+
+int spec_verify_tree_run_point(const spec_verify_ctx* ctx, const spec_verify_tree_args* a,
+                               void* hip_stream) {
+  return run_tree(ctx, a, hip_stream, false);
+}
 
 int spec_verify_create(spec_verify_ctx** out, int device, int64_t vocab, int dtype,
                        int32_t max_seqs, int64_t max_draft_rows, uint32_t flags,

@@ -521,22 +521,14 @@ __device__ __forceinline__ void find_interval(const double* v, int64_t n, double
 // zero-weight logit is never returned).  If rounding leaves tt past the
 // interval's last weight, the last positive-weight logit is returned.  All
 // threads of the workgroup must call it; the result is valid in every
-// thread.
-template <int DT>
-__device__ __forceinline__ int64_t block_search(const GroupRaw<DT>& rp, const GroupRaw<DT>& rq,
-                                                int64_t gi, bool active, const DrawConsts& dd,
-                                                const ExpConsts& ec, double tt, double p_excl,
-                                                DrawShared& ds) {
+// thread.  This core takes the weights each thread already holds (zeros for
+// an inactive thread); block_search below computes them first.
+__device__ __forceinline__ int64_t block_search_weights(const float w[kGroup], int64_t gi,
+                                                        double tt, double p_excl,
+                                                        DrawShared& ds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  float w[kGroup];
-  if (active) {
-    weights_of<DT>(rp, rq, gi * kGroup, dd, ec, w);
-  } else {
-#pragma unroll
-    for (int k = 0; k < kGroup; ++k) w[k] = 0.0f;
-  }
   const double gs = (double)seq_sum8(w);
   const double incl = wave_incl_scan(gs, lane);
   const double below = __shfl_up(incl, 1);
@@ -576,6 +568,21 @@ __device__ __forceinline__ int64_t block_search(const GroupRaw<DT>& rp, const Gr
     lp = ds.last_pos[v] > lp ? ds.last_pos[v] : lp;
   }
   return token >= 0 ? token : lp;
+}
+
+template <int DT>
+__device__ __forceinline__ int64_t block_search(const GroupRaw<DT>& rp, const GroupRaw<DT>& rq,
+                                                int64_t gi, bool active, const DrawConsts& dd,
+                                                const ExpConsts& ec, double tt, double p_excl,
+                                                DrawShared& ds) {
+  float w[kGroup];
+  if (active) {
+    weights_of<DT>(rp, rq, gi * kGroup, dd, ec, w);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) w[k] = 0.0f;
+  }
+  return block_search_weights(w, gi, tt, p_excl, ds);
 }
 
 // Block-wide sum of one double per thread in a fixed order.

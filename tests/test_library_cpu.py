@@ -53,6 +53,24 @@ def test_args_struct_layout_matches_header(tmp_path):
     assert int(got["sizeof"]) == ctypes.sizeof(binding.Args)
 
 
+def test_tree_args_layout_matches_header(tmp_path):
+    fields = [f for f, _ in binding.TreeArgs._fields_]
+    src = tmp_path / "layout3.c"
+    body = "\n".join(
+        f'  printf("{f} %zu\\n", offsetof(spec_verify_tree_args, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "spec_verify.h"\n'
+                   'int main(void){\n' + body +
+                   '\n  printf("sizeof %zu\\n", sizeof(spec_verify_tree_args));\n  return 0;\n}\n')
+    exe = tmp_path / "layout3"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), "-o", str(exe),
+                    str(src)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                 check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(binding.TreeArgs, f).offset, f
+    assert int(got["sizeof"]) == ctypes.sizeof(binding.TreeArgs)
+
+
 def test_adapt_params_layout_matches_header(tmp_path):
     fields = [f for f, _ in binding.AdaptParams._fields_]
     src = tmp_path / "layout2.c"
@@ -105,6 +123,8 @@ def test_host_side_argument_checks_without_a_device():
     assert lib.spec_verify_run(None, None, None) == binding.EINVAL
     assert lib.spec_verify_run_greedy(None, None, None) == binding.EINVAL
     assert lib.spec_verify_run_point_drafts(None, None, None) == binding.EINVAL
+    assert lib.spec_verify_tree_run_greedy(None, None, None) == binding.EINVAL
+    assert lib.spec_verify_tree_run_point(None, None, None) == binding.EINVAL
     assert lib.spec_verify_destroy(None) == binding.OK
     assert lib.spec_verify_workspace_size(None) == 0
     assert lib.spec_verify_num_kernels(None) == 0

@@ -1,0 +1,183 @@
+"""Parity of tree verification (through the C ABI) with the oracle: greedy
+trees bit-exact, point-mass candidates bit-exact outside the oracle's
+flagged 1e-6 ties.  Every case prints its name before touching the GPU."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.gpu_helpers import log, torch_logits
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _verifier(tr, check=False):
+    from rejection_sampling_verify_08_amd import SpecVerifier
+    B, R = tr.num_seqs, tr.rows
+    # row capacity max_seqs + 2 * max_draft_rows >= R
+    return SpecVerifier(tr.vocab, tr.dtype, max_seqs=max(B, 1),
+                        max_draft_rows=max((R - B + 1) // 2, 0), check=check)
+
+
+def _run(tr, mode, sv=None, ld=None, offset=0):
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    sv = sv or _verifier(tr)
+    tgt = torch_logits(tr.target_logits, tr.dtype, "cuda", ld, offset)
+    if mode == "greedy":
+        out = sv.tree_greedy(d(tr.cu_nodes), d(tr.parent), d(tr.tokens), tgt)
+    else:
+        out = sv.tree_point(d(tr.cu_nodes), d(tr.parent), d(tr.tokens), tgt, d(tr.uniforms),
+                            tr.temperature)
+    torch.cuda.synchronize()
+    return (out.out_tokens.cpu().numpy(), out.out_path.cpu().numpy(),
+            out.num_accepted.cpu().numpy(), int(out.status.item()) & 0xFFFFFFFF)
+
+
+def _oracle(tr, mode):
+    if mode == "greedy":
+        return oracle.verify_tree_greedy(tr.num_seqs, tr.cu_nodes, tr.parent, tr.tokens,
+                                         tr.target_logits, vocab=tr.vocab, dtype=tr.dtype)
+    return oracle.verify_tree_point(tr.num_seqs, tr.cu_nodes, tr.parent, tr.tokens,
+                                    tr.target_logits, tr.uniforms, tr.temperature,
+                                    vocab=tr.vocab, dtype=tr.dtype)
+
+
+def _check(tr, mode, label, **kw):
+    log(f"[case] tree {mode} {label}: B={tr.num_seqs} R={tr.rows} V={tr.vocab} {tr.dtype} "
+        f"T={tr.temperature}")
+    ora = _oracle(tr, mode)
+    tok, path, n, st = _run(tr, mode, **kw)
+    assert st == 0, f"{label}: status {st:#x}"
+    bad = []
+    for b in range(tr.num_seqs):
+        g0, g1 = int(tr.cu_nodes[b]), int(tr.cu_nodes[b + 1])
+        same = (n[b] == ora.num_accepted[b] and np.array_equal(tok[g0:g1], ora.out_tokens[g0:g1])
+                and np.array_equal(path[g0:g1], ora.out_path[g0:g1]))
+        if not same and (mode == "greedy" or not ora.flagged[b]):
+            bad.append((b, int(n[b]), int(ora.num_accepted[b])))
+    assert not bad, f"{label}: {len(bad)} sequences differ, first {bad[:3]}"
+    log(f"[parity] tree {mode} {label}: seqs={tr.num_seqs} mean depth "
+        f"{float(ora.num_accepted.mean()):.3f} flagged={int((ora.flagged != 0).sum())}")
+    return ora
+
+
+@pytest.mark.parametrize("mode", ["greedy", "point"])
+def test_tree_workload_full_size(mode):
+    tr = W.tree_config()
+    ora = _check(tr, mode, "128 x 17 nodes V=128256")
+    assert ora.num_accepted.max() >= 1
+
+
+def _mixed_shapes():
+    return ([W.tree_shape(W.TREE_17)] * 3 + [np.asarray([-1], np.int32)] +
+            [W.tree_shape([(1, 64)])] + [W.tree_shape([(1, 1)] * 40)] +
+            [W.tree_shape([(1, 3), (3, 3), (9, 2)])] +
+            [np.asarray([-1, 0, 0, 1, 1, 2, 2, 3, 0], np.int32)])
+
+
+@pytest.mark.parametrize("V", [1, 5, 63, 4097, 32000, 152064])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["greedy", "point"])
+def test_tree_shapes_and_vocab(mode, dtype, V):
+    tr = W.build_tree(f"mixed V{V}", 400 + V, _mixed_shapes(), V, dtype, 0.9,
+                      W.boosted_top_rows(1.0 if mode == "greedy" else 2.0, min(4, V), 6.0), 0.6)
+    _check(tr, mode, f"mixed shapes V={V} {dtype}")
+
+
+@pytest.mark.parametrize("T", [0.7, 1.0, 1.3])
+def test_tree_point_temperatures(T):
+    tr = W.build_tree("temps", 51, [W.tree_shape(W.TREE_17)] * 24, 32000, W.BF16, T,
+                      W.boosted_random_ids_rows(3.0, 20, 8.0), 1.0)
+    _check(tr, "point", f"T={T}")
+
+
+def test_tree_duplicate_and_ragged_candidates():
+    rng = np.random.default_rng(3)
+    tr = W.build_tree("dups", 61, [W.tree_shape([(1, 6), (2, 4)])] * 40, 3000, W.BF16, 1.0,
+                      W.boosted_top_rows(2.0, 3, 5.0), 0.8)
+    tok = tr.tokens.copy()
+    for b in range(tr.num_seqs):          # repeat some sibling tokens
+        g0 = int(tr.cu_nodes[b])
+        if rng.random() < 0.7:
+            tok[g0 + 2] = tok[g0 + 1]
+        if rng.random() < 0.5:
+            tok[g0 + 5] = tok[g0 + 3]
+    tr = dataclasses.replace(tr, tokens=tok)
+    for mode in ("greedy", "point"):
+        _check(tr, mode, "repeated sibling tokens")
+
+
+def test_tree_extreme_uniforms():
+    tr = W.build_tree("uext", 71, [W.tree_shape(W.TREE_17)] * 32, 5000, W.BF16, 1.0,
+                      W.boosted_top_rows(2.0, 4, 6.0), 0.5)
+    u = tr.uniforms.copy()
+    u[0::3] = np.float32(0.0)
+    u[1::3] = np.float32(1 - 2 ** -24)
+    _check(dataclasses.replace(tr, uniforms=u), "point", "u in {0, 1-2^-24}")
+
+
+@pytest.mark.parametrize("ld_extra,offset", [(8, 0), (1, 0), (0, 1)])
+def test_tree_pitch_and_alignment(ld_extra, offset):
+    tr = W.build_tree("pitch", 81, _mixed_shapes(), 4003, W.BF16, 1.0,
+                      W.boosted_top_rows(2.0, 4, 6.0), 0.5)
+    for mode in ("greedy", "point"):
+        _check(tr, mode, f"ld=V+{ld_extra} offset={offset}", ld=tr.vocab + ld_extra, offset=offset)
+
+
+def test_tree_bad_trees_are_skipped():
+    tr = W.build_tree("bad", 91, [W.tree_shape([(1, 3)])] * 4 + [W.tree_shape([(1, 70)])],
+                      500, W.BF16, 1.0, W.iid_normal_rows(1.0), 0.5)
+    par = tr.parent.copy()
+    tok = tr.tokens.copy()
+    par[int(tr.cu_nodes[1]) + 2] = 3          # parent after its child
+    tok[int(tr.cu_nodes[2]) + 1] = 500        # token out of range
+    tr = dataclasses.replace(tr, parent=par, tokens=tok)
+    for mode in ("greedy", "point"):
+        log(f"[case] tree {mode} malformed trees")
+        toks, path, n, st = _run(tr, mode)
+        assert st & 128, hex(st)
+        for b in (1, 2, 4):                   # bad parent, bad token, 70 children
+            g0, g1 = int(tr.cu_nodes[b]), int(tr.cu_nodes[b + 1])
+            assert (toks[g0:g1] == -1).all() and n[b] == 0
+        ora_ok = [0, 3]
+        sub = W.build_tree("bad", 91, [W.tree_shape([(1, 3)])] * 4 + [W.tree_shape([(1, 70)])],
+                           500, W.BF16, 1.0, W.iid_normal_rows(1.0), 0.5)
+        ora = _oracle(sub, mode)
+        for b in ora_ok:
+            g0, g1 = int(tr.cu_nodes[b]), int(tr.cu_nodes[b + 1])
+            if mode == "greedy" or not ora.flagged[b]:
+                assert np.array_equal(toks[g0:g1], ora.out_tokens[g0:g1])
+
+
+def test_tree_point_lossless_one_launch():
+    """10^6 trees in one launch: a root with three candidates (one repeated)
+    whose nodes have children; the token emitted at depth 0 follows p_root
+    and, after node c is accepted, the next token follows p_c."""
+    from scipy import special, stats
+    rng = np.random.default_rng(32)
+    V, N = 6, 1_000_000
+    rows = (rng.standard_normal((7, V)) * 1.1).astype(np.float32)
+    parent = np.asarray([-1, 0, 0, 0, 0, 1, 2], np.int32)
+    tokens = np.asarray([-1, 2, 4, 2, 1, 3, 5], np.int32)
+    p = [special.softmax(r.astype(np.float64)) for r in rows]
+    tr = W.TreeInputs("lossless", V, W.F32, 1.0, np.arange(0, 7 * N + 1, 7, dtype=np.int32),
+                      np.tile(parent, N), np.tile(tokens, N), np.tile(rows, (N, 1)),
+                      W.uniform_grid24(rng, 7 * N))
+    log(f"[case] tree point lossless one launch: B={N}")
+    tok, path, n, st = _run(tr, "point")
+    out, pth = tok.reshape(N, 7), path.reshape(N, 7)
+    level = 1e-3 / 5
+    assert stats.chisquare(np.bincount(out[:, 0], minlength=V), N * p[0]).pvalue > level
+    for node in (1, 2, 4):
+        m = pth[:, 0] == node
+        assert stats.chisquare(np.bincount(out[m, 1], minlength=V), m.sum() * p[node]).pvalue > level
+    assert not (pth[:, 0] == 3).any()
+    ora = _oracle(tr, "point")
+    same = (n == ora.num_accepted) & (out == ora.out_tokens.reshape(N, 7)).all(axis=1)
+    log(f"[parity] tree point lossless: differing={int((~same).sum())} "
+        f"flagged={int((ora.flagged != 0).sum())}")
+    assert (same | (ora.flagged != 0)).all()

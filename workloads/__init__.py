@@ -340,9 +340,10 @@ def tree_shape(levels) -> np.ndarray:
 def build_tree(name: str, seed: int, shapes, vocab: int, dtype: str, temperature: float,
                target_row: RowFn, draft_sd: float, workers: Optional[int] = None) -> TreeInputs:
     """Candidate trees: sequence b has the local parent array shapes[b].  A
-    node's children carry the top tokens (largest first, distinct) of a draft
-    row made of the node's float64 target row plus N(0, draft_sd^2) noise --
-    a drafter proposing its top-k at each expanded node.  Seeding as in
+    node's children carry the top tokens (largest first, distinct while the
+    vocabulary allows) of a draft row made of the node's float64 target row
+    plus N(0, draft_sd^2) noise -- a drafter proposing its top-k at each
+    expanded node.  Seeding as in
     build(): SeedSequence(seed).spawn(6), one child per row for the target,
     boost and draft-noise streams."""
     ss = np.random.SeedSequence(seed).spawn(6)
@@ -369,7 +370,8 @@ def build_tree(name: str, seed: int, shapes, vocab: int, dtype: str, temperature
             if kids.size:
                 d = t64 + r_draft[g0 + n].standard_normal(vocab) * draft_sd
                 top = np.argsort(-d, kind="stable")[:kids.size]
-                tokens[g0 + kids] = top.astype(np.int32)
+                # fewer tokens than children (tiny vocabularies): repeat them
+                tokens[g0 + kids] = np.resize(top, kids.size).astype(np.int32)
 
     n_work = workers or min(16, os.cpu_count() or 1)
     if R * vocab < (1 << 18) or n_work <= 1:
