@@ -41,6 +41,7 @@ namespace sv {
 
 constexpr int kMaxTreeNodes = 1024;
 constexpr int kMaxChildren = 64;
+constexpr int kXBatch = 4;        // child-token tasks loaded per round
 
 struct TreeNodes {
   int32_t par[kMaxTreeNodes];
@@ -194,35 +195,33 @@ struct TreePointShared {
   float wx[kMaxChildren];        // w of each distinct token in the node's scale
   int32_t xtask[kMaxChildren];   // distinct tasks holding those tokens
   double xsum[kMaxChildren];     // exact sums of those tasks without the tokens
+  double red[kWaves][kXBatch];   // per-wave partial sums of a batch of tasks
   int nkids, nx, ntask;
   int next;                      // accepted child, or -1
-  int have_x;                    // xsum / xs hold the current node's values
-  double rest_x;                 // mass of the row without the children's tokens
+  int empty;                     // the final weights summed to 0
 };
 
-// One block pass over task `task` of row `prow` (thread t < 512 holds group
-// task * 512 + t): weights 2^(l c + Ap), zero at the listed tokens.
-template <int DT, bool VEC>
-__device__ __forceinline__ void task_weights_without(const void* prow, int64_t task, int64_t V,
-                                                     float Ap, const ExpConsts& ec,
-                                                     const int32_t* excl, int nexcl,
-                                                     float w[kGroup], int64_t& gi, bool& active) {
-  constexpr int64_t kTaskGroups = kWaveTaskElems / kGroup;
-  active = threadIdx.x < kTaskGroups;
-  gi = task * kTaskGroups + threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < kGroup; ++k) w[k] = 0.0f;
-  if (!active) return;
-  GroupRaw<DT> r;
-  load_group<DT, VEC>(prow, gi, V, r);
+// Weights of one group of row `prow` in the scale 2^(l c + Ap), zero at the
+// listed tokens.
+template <int DT>
+__device__ __forceinline__ void group_weights_without(const GroupRaw<DT>& r, int64_t gi,
+                                                      float Ap, const ExpConsts& ec,
+                                                      const int32_t* excl, int nexcl,
+                                                      float w[kGroup]) {
   float v[kGroup];
   unpack<DT>(r, v);
 #pragma unroll
-  for (int k = 0; k < kGroup; ++k) {
-    const int64_t e = gi * kGroup + k;
-    bool out = false;
-    for (int i = 0; i < nexcl; ++i) out = out || (excl[i] == e);
-    w[k] = out ? 0.0f : exp_term(v[k], Ap, ec);
+  for (int k = 0; k < kGroup; ++k) w[k] = exp_term(v[k], Ap, ec);
+  // one (wave-uniform) read per listed token; only the thread whose group
+  // holds it clears that weight
+  const int64_t base = gi * kGroup;
+  for (int i = 0; i < nexcl; ++i) {
+    const int64_t d = (int64_t)excl[i] - base;
+    if (d >= 0 && d < kGroup) {
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k)
+        if (k == d) w[k] = 0.0f;
+    }
   }
 }
 
@@ -239,7 +238,8 @@ __global__ __launch_bounds__(kThreads) void tree_point_kernel(
   extern __shared__ double lds_dyn[];   // [2 * tpr]: converted task sums, draw sums
   double* task_sum = lds_dyn;
   double* draw_sum = lds_dyn + tpr;
-  constexpr int64_t kTaskGroups = kWaveTaskElems / kGroup;
+  constexpr int64_t kTaskGroups = kWaveTaskElems / kGroup;   // 512 = one group per thread
+  static_assert(kTaskGroups == kThreads, "a task is one group per thread");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -253,46 +253,75 @@ __global__ __launch_bounds__(kThreads) void tree_point_kernel(
                           out_tokens, out_path, out_num_accepted, status);
     return;
   }
+  for (int64_t n = tid; n < N; n += kThreads) sh.u[n] = uniforms[g0 + n];
   load_tree<kThreads>(parent, tokens, g0, N, V, sh.tn);
   if (sh.tn.bad) {
     reject_tree<kThreads>(b, g0, N, true, SPEC_VERIFY_DEV_BAD_TREE, out_tokens, out_path,
                           out_num_accepted, status);
     return;
   }
-  // every node's row normaliser, its token's logit in the parent's row, its
-  // uniform
+  // ---- every node's row normaliser and its token's logit in the parent's
+  // row; the loads of two row passes and of the logits are issued before any
+  // is reduced
   {
     const int L = combine_lanes;
     const int rows_per_wave = 64 / L;
-    for (int64_t n = tid; n < N; n += kThreads) {
-      sh.u[n] = uniforms[g0 + n];
-      sh.lx[n] = n == 0 ? 0.0f
-                        : load_logit<DT>(row_ptr<DT>(target, g0 + sh.tn.par[n], ld), sh.tn.tok[n]);
+    const int64_t stride = (int64_t)kWaves * rows_per_wave;
+    float lxv[2];
+    for (int64_t n0 = 0; n0 < N; n0 += 2 * kThreads) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t n = n0 + h * kThreads + tid;
+        lxv[h] = (n >= 1 && n < N)
+                     ? load_logit<DT>(row_ptr<DT>(target, g0 + sh.tn.par[n], ld), sh.tn.tok[n])
+                     : 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t n = n0 + h * kThreads + tid;
+        if (n < N) sh.lx[n] = lxv[h];
+      }
     }
-    for (int64_t r0 = (int64_t)wave * rows_per_wave; r0 < N;
-         r0 += (int64_t)kWaves * rows_per_wave) {
-      const int64_t r = r0 + lane / L;
-      const bool active = (lane / L) < rows_per_wave && r < N;
-      const RowNorm rn = tpr <= L
-          ? reduce_partials(load_partial(part, tpr, active ? g0 + r : 0, lane & (L - 1), active),
-                            L, ec)
-          : combine_rows_packed(part, tpr, L, active ? g0 + r : 0, active, ec, lane);
+    auto store = [&](int64_t r, bool active, const RowNorm& rn) {
       if (active && (lane & (L - 1)) == 0) {
         sh.M[r] = rn.M;
         sh.s[r] = rn.s;
+      }
+    };
+    if (tpr <= L) {
+      for (int64_t r0 = (int64_t)wave * rows_per_wave; r0 < N; r0 += 2 * stride) {
+        const int64_t ra = r0 + lane / L, rb = ra + stride;
+        const bool act_a = (lane / L) < rows_per_wave && ra < N;
+        const bool act_b = (lane / L) < rows_per_wave && rb < N;
+        const Partial pa = load_partial(part, tpr, act_a ? g0 + ra : 0, lane & (L - 1), act_a);
+        const Partial pb = load_partial(part, tpr, act_b ? g0 + rb : 0, lane & (L - 1), act_b);
+        store(ra, act_a, reduce_partials(pa, L, ec));
+        store(rb, act_b, reduce_partials(pb, L, ec));
+      }
+    } else {
+      for (int64_t r0 = (int64_t)wave * rows_per_wave; r0 < N; r0 += stride) {
+        const int64_t r = r0 + lane / L;
+        const bool active = (lane / L) < rows_per_wave && r < N;
+        store(r, active, combine_rows_packed(part, tpr, L, active ? g0 + r : 0, active, ec, lane));
       }
     }
   }
   if (tid == 0) sh.tn.depth = 0;
   __syncthreads();
 
+  // The groups of the last batch of child-token tasks stay in registers: the
+  // final search reuses them when it lands in one of those tasks.
+  GroupRaw<DT> xraw[kXBatch];
+  int32_t xraw_task[kXBatch];
+#pragma unroll
+  for (int j = 0; j < kXBatch; ++j) xraw_task[j] = -1;
   uint32_t fbad = 0;
   int64_t cur = 0;
   for (;;) {
     const void* prow = row_ptr<DT>(target, g0 + cur, ld);
     const float Ap = shift_of(sh.M[cur], ec);
-    // ---- the current node's children in index order, and its task sums
-    // moved into the draw's scale 2^(l c + Ap)
+    // ---- the current node's children in index order, their distinct tokens
+    // and the tasks holding them (wave 0)
     if (wave == 0) {
       int cnt = 0;
       for (int64_t base = cur + 1; base < N; base += 64) {
@@ -303,32 +332,8 @@ __global__ __launch_bounds__(kThreads) void tree_point_kernel(
         cnt += __builtin_popcountll(m);
       }
       if (lane == 0) {
-        sh.nkids = cnt;
-        sh.next = -1;
-        sh.have_x = 0;
-      }
-    }
-    const Partial* prt = part + (g0 + cur) * tpr;
-    for (int64_t c = tid; c < tpr; c += kThreads) {
-      const Partial pc = prt[c];
-      task_sum[c] = pc.m == -INFINITY ? 0.0 : pc.s * exp2((double)Ap - (double)shift_of(pc.m, ec));
-    }
-    __syncthreads();
-    const int nk = sh.nkids;
-    // ---- the first child: nothing removed yet, p' = p ([A] 1.2 step 3 with
-    // q the point mass at the candidate)
-    if (tid == 0 && nk > 0) {
-      const int32_t c = sh.kids[0];
-      const double r = exp(((double)sh.lx[c] - (double)sh.M[cur]) / ec.T) / sh.s[cur];
-      if ((double)sh.u[c] < r) sh.next = c;
-    }
-    __syncthreads();
-    // ---- the children's tokens, their weights and the exact mass without
-    // them (needed by every later sibling and by the final draw)
-    if (sh.next < 0 && nk > 0) {
-      if (tid == 0) {
         int nx = 0, nt = 0;
-        for (int i = 0; i < nk; ++i) {
+        for (int i = 0; i < cnt; ++i) {
           const int32_t c = sh.kids[i];
           const int32_t x = sh.tn.tok[c];
           bool seen = false;
@@ -342,61 +347,91 @@ __global__ __launch_bounds__(kThreads) void tree_point_kernel(
           for (int j = 0; j < nt; ++j) tseen = tseen || sh.xtask[j] == t;
           if (!tseen) sh.xtask[nt++] = t;
         }
+        sh.nkids = cnt;
         sh.nx = nx;
         sh.ntask = nt;
+        sh.next = -1;
+      }
+    }
+    __syncthreads();
+    const int nk = sh.nkids, nx = sh.nx, ntask = sh.ntask;
+    // ---- one round of loads: the row's task partials and the groups of the
+    // tasks holding child tokens; then the task sums in the draw's scale
+    // 2^(l c + Ap) and those tasks summed without the child tokens
+    const Partial* prt = part + (g0 + cur) * tpr;
+    for (int64_t j0 = 0; j0 < (ntask > 0 ? ntask : 1); j0 += kXBatch) {
+      const int nb = ntask - (int)j0 < kXBatch ? ntask - (int)j0 : kXBatch;
+#pragma unroll
+      for (int j = 0; j < kXBatch; ++j) {
+        xraw_task[j] = j < nb ? sh.xtask[j0 + j] : -1;
+        if (j < nb) load_group<DT, VEC>(prow, (int64_t)xraw_task[j] * kTaskGroups + tid, V, xraw[j]);
+      }
+      if (j0 == 0)
+        for (int64_t c = tid; c < tpr; c += kThreads) {
+          const Partial pc = prt[c];
+          task_sum[c] = pc.m == -INFINITY ? 0.0
+                                          : pc.s * exp2((double)Ap - (double)shift_of(pc.m, ec));
+        }
+#pragma unroll
+      for (int j = 0; j < kXBatch; ++j) {
+        double gs = 0.0;
+        if (j < nb) {
+          float w[kGroup];
+          group_weights_without<DT>(xraw[j], (int64_t)xraw_task[j] * kTaskGroups + tid, Ap, ec,
+                                    sh.xs, nx, w);
+          gs = (double)seq_sum8(w);
+        }
+        gs = __shfl(wave_incl_scan(gs, lane), 63);
+        if (lane == 0) sh.red[wave][j] = gs;
       }
       __syncthreads();
-      for (int j = 0; j < sh.ntask; ++j) {
-        float w[kGroup];
-        int64_t gi;
-        bool active;
-        task_weights_without<DT, VEC>(prow, sh.xtask[j], V, Ap, ec, sh.xs, sh.nx, w, gi, active);
-        const double ts = block_sum((double)seq_sum8(w), ds);
-        if (tid == 0) sh.xsum[j] = ts;
-        __syncthreads();   // ds.red is reused
-      }
-      if (wave == 0) {
-        // draw sums: task sums, with the children's tasks summed without them
-        for (int64_t c = lane; c < tpr; c += 64) {
-          double v = task_sum[c];
-          for (int j = 0; j < sh.ntask; ++j)
-            if (sh.xtask[j] == c) v = sh.xsum[j];
-          draw_sum[c] = v;
-        }
-        const double rest = wave_total(draw_sum, tpr, lane);
-        if (lane == 0) {
-          sh.rest_x = rest;
-          sh.have_x = 1;
-        }
+      if (tid < nb) {
+        double t = 0.0;
+        for (int v = 0; v < kWaves; ++v) t += sh.red[v][tid];
+        sh.xsum[j0 + tid] = t;
       }
       __syncthreads();
-      // ---- later siblings: p'(x) = w(x) / (mass without the children's
-      // tokens + the children's tokens not yet rejected)
-      if (tid == 0) {
+    }
+    // ---- wave 0: the mass without the children's tokens, then the tests
+    // in index order.  The first child sees p' = p ([A] 1.2 step 3 with q
+    // the point mass at the candidate); each later one p without the tokens
+    // already rejected: p'(x) = w(x) / (mass without every child token + the
+    // child tokens not yet rejected).
+    if (wave == 0 && nk > 0) {
+      for (int64_t c = lane; c < tpr; c += 64) {
+        double v = task_sum[c];
+        for (int j = 0; j < ntask; ++j)
+          if (sh.xtask[j] == c) v = sh.xsum[j];
+        draw_sum[c] = v;
+      }
+      const double rest_x = wave_total(draw_sum, tpr, lane);
+      if (lane == 0) {
         uint64_t removed = 0;   // bit j: xs[j] rejected
         for (int i = 0; i < nk; ++i) {
           const int32_t c = sh.kids[i];
           const int32_t x = sh.tn.tok[c];
           int jx = 0;
           while (sh.xs[jx] != x) ++jx;
-          if (i > 0) {
-            double r = 0.0;
-            if (!((removed >> jx) & 1)) {
-              double rest = sh.rest_x;
-              for (int j = 0; j < sh.nx; ++j)
-                if (!((removed >> j) & 1)) rest += (double)sh.wx[j];
-              r = rest > 0.0 ? (double)sh.wx[jx] / rest : 0.0;
-            }
-            if ((double)sh.u[c] < r) {
-              sh.next = c;
-              break;
-            }
+          double r;
+          if (i == 0) {
+            r = exp(((double)sh.lx[c] - (double)sh.M[cur]) / ec.T) / sh.s[cur];
+          } else if ((removed >> jx) & 1) {
+            r = 0.0;
+          } else {
+            double rest = rest_x;
+            for (int j = 0; j < nx; ++j)
+              if (!((removed >> j) & 1)) rest += (double)sh.wx[j];
+            r = rest > 0.0 ? (double)sh.wx[jx] / rest : 0.0;
+          }
+          if ((double)sh.u[c] < r) {
+            sh.next = c;
+            break;
           }
           removed |= 1ull << jx;
         }
       }
-      __syncthreads();
     }
+    __syncthreads();
     if (sh.next >= 0) {
       if (tid == 0) sh.tn.path[sh.tn.depth++] = sh.next;
       cur = sh.next;
@@ -411,32 +446,41 @@ __global__ __launch_bounds__(kThreads) void tree_point_kernel(
   const int nk = sh.nkids;
   const void* prow = row_ptr<DT>(target, g0 + cur, ld);
   const float Ap = shift_of(sh.M[cur], ec);
-  const double* sums = nk > 0 ? draw_sum : task_sum;
   if (wave == 0) {
+    const double* sums = nk > 0 ? draw_sum : task_sum;
     double total = wave_total(sums, tpr, lane);
+    int empty = 0;
     if (!(total > 0.0)) {
       // empty residual (invalid input or extreme rounding): draw from p
-      if (lane == 0) ds.empty = 1;
+      empty = 1;
       sums = task_sum;
       total = wave_total(sums, tpr, lane);
-    } else if (lane == 0) {
-      ds.empty = 0;
     }
     const double tt = (double)sh.u[0] * total;
     find_interval(sums, tpr, tt, lane, ds);
-    if (lane == 0) ds.tt = tt;
+    if (lane == 0) {
+      ds.tt = tt;
+      sh.empty = empty;
+    }
   }
   __syncthreads();
-  const bool exclude = nk > 0 && !ds.empty;
-  if (ds.empty) fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
+  const bool exclude = nk > 0 && !sh.empty;
+  if (sh.empty) fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
   const int64_t tau = ds.tau;
   int64_t token = -1;
   if (tau >= 0) {
+    GroupRaw<DT> r;
+    bool have = false;
+#pragma unroll
+    for (int j = 0; j < kXBatch; ++j)
+      if (xraw_task[j] == tau) {
+        r = xraw[j];
+        have = true;
+      }
+    const int64_t gi = tau * kTaskGroups + tid;
+    if (!have) load_group<DT, VEC>(prow, gi, V, r);
     float w[kGroup];
-    int64_t gi;
-    bool active;
-    task_weights_without<DT, VEC>(prow, tau, V, Ap, ec, sh.xs, exclude ? sh.nx : 0, w, gi,
-                                  active);
+    group_weights_without<DT>(r, gi, Ap, ec, sh.xs, exclude ? sh.nx : 0, w);
     const double tt = ds.tt, p_excl = ds.p_excl;
     __syncthreads();   // ds is reused by the search
     token = block_search_weights(w, gi, tt, p_excl, ds);
@@ -446,7 +490,6 @@ __global__ __launch_bounds__(kThreads) void tree_point_kernel(
     out_num_accepted[b] = sh.tn.depth;
     status_or(status, fbad);
   }
-  (void)kTaskGroups;
 }
 
 }  // namespace sv
