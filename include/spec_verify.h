@@ -92,7 +92,11 @@ extern "C" {
                                       pointers, wrong device, bad sizes */
 #define SPEC_VERIFY_EUNSUPPORTED -2 /* dtype not f32/bf16, V <= 0, V > 2^21 */
 #define SPEC_VERIFY_ECAPACITY -3   /* B > max_seqs, R_d > max_draft_rows,
-                                      workspace smaller than required */
+                                      workspace smaller than required, or a
+                                      batch so large that a launch would
+                                      exceed 2^32 threads (rows * ceil(V /
+                                      4096) * 64, or B * 512 per finishing
+                                      workgroup) */
 #define SPEC_VERIFY_EHIP -4        /* a HIP call failed; see
                                       spec_verify_last_hip_error() */
 

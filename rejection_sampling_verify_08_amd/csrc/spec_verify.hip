@@ -202,6 +202,17 @@ hipError_t dispatch_vec(const spec_verify_ctx* ctx, const spec_verify_args* a,
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// A launch's total thread count must stay below 2^32: the row pass runs one
+// wave per 4096-logit task of `rows` rows, the finishing kernels at most
+// cu_count / B (>= 1) workgroups of kThreads per sequence.
+bool grids_fit(const spec_verify_ctx* ctx, int64_t rows, int64_t B) {
+  const int64_t limit = (int64_t)1 << 32;
+  if (rows > limit / 64 / ctx->tasks_per_row) return false;
+  int64_t G = B > 0 ? ctx->cu_count / B : 1;
+  if (G < 1) G = 1;
+  return B <= limit / sv::kThreads / G;
+}
+
 // Host-side argument checks shared by the three entry points, then the
 // launches.  Fields a mode does not use are not checked.
 int run_mode(const spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_stream,
@@ -216,6 +227,7 @@ int run_mode(const spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_st
     return SPEC_VERIFY_EINVAL;
   if (a->ld < ctx->vocab) return SPEC_VERIFY_EINVAL;
   if (B > ctx->max_seqs || R_d > ctx->max_draft_rows) return SPEC_VERIFY_ECAPACITY;
+  if (!grids_fit(ctx, 2 * R_d + B, B)) return SPEC_VERIFY_ECAPACITY;
   if (B == 0) return SPEC_VERIFY_OK;
   const size_t esize = ctx->dtype == SPEC_VERIFY_BF16 ? 2 : 4;
   if (!a->cu_draft || !a->target_logits || !a->out_tokens || !a->out_num_accepted ||
@@ -304,6 +316,7 @@ int run_tree(const spec_verify_ctx* ctx, const spec_verify_tree_args* a, void* h
   if (a->ld < ctx->vocab) return SPEC_VERIFY_EINVAL;
   if (B > ctx->max_seqs || R > (int64_t)ctx->max_seqs + 2 * ctx->max_draft_rows)
     return SPEC_VERIFY_ECAPACITY;
+  if (!grids_fit(ctx, R, B)) return SPEC_VERIFY_ECAPACITY;
   if (B == 0) return SPEC_VERIFY_OK;
   if (R < B) return SPEC_VERIFY_EINVAL;   // every tree has a root
   const size_t esize = ctx->dtype == SPEC_VERIFY_BF16 ? 2 : 4;
