@@ -228,3 +228,27 @@ def test_lossless_on_gpu_one_launch():
     log(f"[parity] lossless one launch: seqs={N} flagged={int(flagged.sum())} "
         f"differing={int((~same).sum())}")
     assert (same | flagged).all()
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configurations(seed):
+    """Seeded random shapes: vocabulary, batch, ragged gammas (up to 20), dtype,
+    temperature, row generator, draft noise and a padded pitch."""
+    rng = np.random.default_rng(10_000 + seed)
+    V = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 9000)),
+                        int(rng.integers(9000, 70000))]))
+    B = int(rng.integers(1, 40))
+    gam = rng.integers(0, 21, size=B)
+    dtype = W.BF16 if rng.random() < 0.6 else W.F32
+    T = float(rng.uniform(0.5, 1.5))
+    gen = [W.iid_normal_rows(float(rng.uniform(0.3, 3.0))),
+           W.boosted_top_rows(2.0, max(1, min(50, V // 3)), 6.0),
+           W.boosted_random_ids_rows(3.0, max(1, min(20, V)), 8.0)][int(rng.integers(0, 3))]
+    inp = W.build(f"random {seed}", 20_000 + seed, gam, V, dtype, T, gen,
+                  float(rng.uniform(0.0, 2.0)))
+    ld = V + int(rng.integers(0, 3)) * 8
+    log(f"[case] random {seed}: B={B} V={V} {dtype} T={T:.3f} ld={ld} max gamma={int(gam.max())}")
+    ora = oracle.verify_inputs(inp)
+    gpu = run_gpu(inp, ld=ld)
+    compare(inp, gpu, ora, label=f"random {seed}")
+    assert gpu.status == 0

@@ -259,3 +259,18 @@ def test_modes_share_one_context_and_workspace():
         got = run_gpu(inp, sv=sv, dev_inputs=d, mode=m)
         np.testing.assert_array_equal(got.out_tokens, ref[m].out_tokens, err_msg=m)
         np.testing.assert_array_equal(got.num_accepted, ref[m].num_accepted, err_msg=m)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations_greedy_and_point(seed):
+    rng = np.random.default_rng(30_000 + seed)
+    V = int(rng.integers(1, 40000))
+    B = int(rng.integers(1, 40))
+    gam = rng.integers(0, 21, size=B)
+    dtype = W.BF16 if rng.random() < 0.6 else W.F32
+    T = float(rng.uniform(0.5, 1.5))
+    inp = W.with_deterministic_drafts(
+        W.build(f"random {seed}", 40_000 + seed, gam, V, dtype, T,
+                W.boosted_top_rows(1.0, max(1, min(5, V)), 5.0), float(rng.uniform(0.0, 1.0))))
+    _greedy(inp, f"random {seed} V={V} {dtype}")
+    _point(inp, f"random {seed} V={V} {dtype} T={T:.3f}")

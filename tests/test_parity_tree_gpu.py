@@ -181,3 +181,30 @@ def test_tree_point_lossless_one_launch():
     log(f"[parity] tree point lossless: differing={int((~same).sum())} "
         f"flagged={int((ora.flagged != 0).sum())}")
     assert (same | (ora.flagged != 0)).all()
+
+
+def _random_tree(rng, max_nodes):
+    n = int(rng.integers(1, max_nodes + 1))
+    parent = [-1]
+    kids = [0]
+    for i in range(1, n):
+        cand = [j for j in range(i) if kids[j] < 64]
+        p = int(cand[int(rng.integers(0, len(cand)))] if rng.random() < 0.5 else cand[-1])
+        parent.append(p)
+        kids[p] += 1
+        kids.append(0)
+    return np.asarray(parent, np.int32)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_trees(seed):
+    rng = np.random.default_rng(50_000 + seed)
+    V = int(rng.integers(2, 30000))
+    B = int(rng.integers(1, 24))
+    shapes = [_random_tree(rng, int(rng.choice([3, 20, 120]))) for _ in range(B)]
+    dtype = W.BF16 if rng.random() < 0.6 else W.F32
+    tr = W.build_tree(f"random tree {seed}", 60_000 + seed, shapes, V, dtype,
+                      float(rng.uniform(0.6, 1.4)), W.boosted_top_rows(1.5, max(1, min(4, V)), 6.0),
+                      float(rng.uniform(0.0, 1.0)))
+    for mode in ("greedy", "point"):
+        _check(tr, mode, f"random trees {seed} V={V} {dtype}")
