@@ -10,8 +10,11 @@ reads logits the previous step left in the 256 MB Infinity Cache.
 
 Prints one JSON line: verified rows/s (value), whole-step HBM GB/s, the
 roofline of the dominant kernel (the row-statistics pass, HBM-bound; its
-duration from HIP events recorded on the launch stream around each kernel),
-and the float64 CPU oracle timed on this host as a reported baseline.
+duration from HIP events that are its dispatch's own start and stop), the
+per-step GPU time's p10/p50/p90, the step time without rotating the inputs
+("unflushed"), the practical read ceiling measured by a streaming-read probe
+over 1 GiB with the row pass's load pattern, and the float64 CPU oracle
+timed on this host as a reported baseline.
 
 The same line carries, under "modes", the same measurement for the two other
 entry points on the same batch with deterministic drafts (each draft token
@@ -112,6 +115,9 @@ def main() -> int:
                     help="record per-kernel timing events on every n-th timed step")
     ap.add_argument("--skip-modes", action="store_true",
                     help="time only spec_verify_run (not the greedy and point-draft entry points)")
+    ap.add_argument("--read-probe-mib", type=int, default=1024,
+                    help="size of the streaming-read probe (the practical read ceiling, "
+                         "0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run three plain device-to-device copies of this "
                          "many MiB (a known-size reference for HBM byte counters)")
@@ -186,6 +192,12 @@ def main() -> int:
         ms = (t1 - t0) * 1e3 / a.steps
         k_ms = [[ev[i][2 * k].elapsed_time(ev[i][2 * k + 1]) for i in steps_ev]
                 for k in range(nk)]
+        # per-step GPU span: first kernel's start to the last kernel's stop
+        span = [ev[i][0].elapsed_time(ev[i][2 * nk - 1]) for i in steps_ev]
+        pct = {"p10": float(np.percentile(span, 10)), "p50": float(np.percentile(span, 50)),
+               "p90": float(np.percentile(span, 90))}
+        timed.last_pct = {k: round(v * 1e3, 2) for k, v in pct.items()}
+        timed.last_kernel_p50 = [round(float(np.percentile(x, 50)) * 1e3, 2) for x in k_ms]
         return ms, [sum(x) / len(x) for x in k_ms]
 
     def sampled_step(i, events):
@@ -194,6 +206,38 @@ def main() -> int:
            timing_events=events)
 
     ms_step, k_avg = timed(sampled_step)
+    step_pct, k_p50 = timed.last_pct, timed.last_kernel_p50
+
+    # the same call without rotating the inputs: part of each step's rows can
+    # then still be in the 256 MB Infinity Cache from the step before
+    def unflushed_step(i, events):
+        t, d = sets[0]
+        sv(cu, t, d, tok, uni, inp.temperature, out=outs[0], stream=stream, timing_events=events)
+
+    ms_unflushed, _ = timed(unflushed_step)
+
+    # the practical read ceiling: one streaming read of a buffer far larger
+    # than the Infinity Cache, with the row pass's load pattern
+    probe = None
+    if a.read_probe_mib > 0:
+        from rejection_sampling_verify_08_amd.binding import read_probe
+        nb = a.read_probe_mib << 20
+        buf = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(7)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        probe = {"bytes": nb, "kernel": "read_probe_kernel",
+                 "loads": "16-byte, one 1 KB span per wave instruction (the row pass's pattern)"}
+        for nt, key in ((True, "nontemporal_gbps"), (False, "plain_gbps")):
+            for _ in range(3):
+                read_probe(buf, sink, nontemporal=nt, stream=stream)
+            runs = [make_events(2) for _ in range(10)]
+            torch.cuda.synchronize()
+            for e in runs:
+                read_probe(buf, sink, nontemporal=nt, stream=stream, events=e)
+            torch.cuda.synchronize()
+            gbps = sorted(nb / (e[0].elapsed_time(e[1]) / 1e3) / 1e9 for e in runs)
+            probe[key] = round(float(np.median(gbps)), 1)
+            probe[key.replace("gbps", "best_gbps")] = round(gbps[-1], 1)
+        del buf
 
     if a.copy_probe_mib > 0:
         n = a.copy_probe_mib << 20
@@ -219,6 +263,8 @@ def main() -> int:
             "traffic": traffic, "kernel": "row_stats_kernel",
             "kernel_avg_us": round(k_avg[0] * 1e3, 2),
             "algorithmic_bytes_per_launch": first}
+    if probe:
+        roof["frac_of_read_probe"] = round(achieved / probe["nontemporal_gbps"], 4)
 
     # the other two entry points on the same target rows, deterministic drafts
     modes = {}
@@ -352,9 +398,12 @@ def main() -> int:
         "hbm_gbps": round(hbm, 1), "hbm_frac": round(hbm / PEAK_HBM_GBPS, 4),
         "step_algorithmic_bytes": step_bytes,
         "kernel_avg_us": [round(x * 1e3, 2) for x in k_avg],
+        "kernel_p50_us": k_p50,
         "kernel_names": ["row_stats_kernel", "finish_kernel"][:nk],
+        "step_gpu_us": step_pct,
+        "unflushed_ms_per_step": round(ms_unflushed, 5),
         "mean_accepted": round(float(num_acc.mean()), 4), "status": status,
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "read_probe": probe, "cpu_baseline": cpu,
         "modes": modes or None,
         "adaptive_draft_length": adapt,
         "kernel_source_hash": src_hash,

@@ -321,6 +321,22 @@ SPEC_VERIFY_API const char *spec_verify_status_string(int status);
 /* The hipError_t of the last EHIP failure on the calling thread (0 if none). */
 SPEC_VERIFY_API int spec_verify_last_hip_error(void);
 
+/*
+ * Measurement only, not part of the verify step: one streaming read of
+ * `bytes` of device memory at `src` with the row pass's load pattern (one
+ * wave per 8 KB, 16-byte loads, each load instruction covering 1 KB of
+ * contiguous memory; non-temporal loads when `nontemporal` is nonzero), to
+ * measure the chip's practical read bandwidth next to the row pass.  `src`
+ * is 16-byte aligned and `bytes` a nonzero multiple of 8192; `sink` is one
+ * device uint32 that is written only if the data folds (XOR) to 0x9E3779B9.
+ * start_event / stop_event (hipEvent_t created with timing, both or
+ * neither) become the kernel's own dispatch start / stop events.  Enqueues
+ * one kernel on `hip_stream`; returns OK, EINVAL, ECAPACITY or EHIP.
+ */
+SPEC_VERIFY_API int spec_verify_read_probe(const void *src, size_t bytes, int nontemporal,
+                                           uint32_t *sink, void *hip_stream,
+                                           void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ EXPORTED = ("spec_verify_create", "spec_verify_query_workspace",
             "spec_verify_run_greedy", "spec_verify_run_point_drafts",
             "spec_verify_tree_run_greedy", "spec_verify_tree_run_point",
             "spec_verify_destroy", "spec_verify_status_string",
-            "spec_verify_last_hip_error",
+            "spec_verify_last_hip_error", "spec_verify_read_probe",
             "spec_verify_adapt_preset", "spec_verify_adapt_state_bytes",
             "spec_verify_adapt_reset", "spec_verify_adapt_update")
 
@@ -170,6 +170,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_last_hip_error.restype = ctypes.c_int
     lib.spec_verify_last_hip_error.argtypes = []
+    lib.spec_verify_read_probe.restype = ctypes.c_int
+    lib.spec_verify_read_probe.argtypes = [P, ctypes.c_size_t, ctypes.c_int, P, P, P, P]
     _lib = lib
     return lib
 
@@ -403,6 +405,25 @@ def verify(cu_draft, target_logits, draft_logits, draft_tokens, uniforms,
     sv = SpecVerifier(V, target_logits.dtype, max_seqs=max(B, 1),
                       max_draft_rows=R_d, device=target_logits.device, check=check)
     return sv(cu_draft, target_logits, draft_logits, draft_tokens, uniforms, temperature)
+
+
+def read_probe(src, sink, *, nontemporal: bool = True, stream=None, events=None) -> None:
+    """Enqueue spec_verify_read_probe over the bytes of the CUDA tensor `src`
+    (measurement only).  `sink` is a one-element int32 CUDA tensor; `events`
+    an optional (start, stop) pair of timing-enabled torch.cuda.Event that
+    have been recorded once (so the HIP events exist)."""
+    import torch
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    handle = (stream or torch.cuda.current_stream()).cuda_stream
+    ev = (None, None)
+    if events is not None:
+        ev = tuple(int(e.cuda_event) for e in events)
+    st = lib.spec_verify_read_probe(ctypes.c_void_p(src.data_ptr()), nbytes, int(nontemporal),
+                                    ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(handle),
+                                    ctypes.c_void_p(ev[0]), ctypes.c_void_p(ev[1]))
+    if st != OK:
+        raise SpecVerifyError("spec_verify_read_probe", st, lib.spec_verify_last_hip_error())
 
 
 def adapt_params(preset: str = "window50", **overrides) -> AdaptParams:

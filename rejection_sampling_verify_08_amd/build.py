@@ -18,6 +18,7 @@ HEADERS = [os.path.join(PKG, "csrc", "spec_verify_kernels.hpp"),
            os.path.join(PKG, "csrc", "greedy_kernels.hpp"),
            os.path.join(PKG, "csrc", "tree_kernels.hpp"),
            os.path.join(PKG, "csrc", "adaptive_k.hpp"),
+           os.path.join(PKG, "csrc", "read_probe.hpp"),
            os.path.join(ROOT, "include", "spec_verify_adapt.h"),
            os.path.join(ROOT, "include", "spec_verify.h")]
 LIB_DIR = os.path.join(PKG, "lib")

@@ -17,6 +17,7 @@
 #include "greedy_kernels.hpp"
 #include "tree_kernels.hpp"
 #include "adaptive_k.hpp"
+#include "read_probe.hpp"
 
 static_assert(sv::kMaxTreeNodes == SPEC_VERIFY_MAX_TREE_NODES, "tree node limit");
 static_assert(sv::kMaxChildren == SPEC_VERIFY_MAX_TREE_CHILDREN, "tree child limit");
@@ -289,7 +290,8 @@ hipError_t launch_tree(const spec_verify_ctx* ctx, const spec_verify_tree_args* 
              stream, ev, 0, a->target_logits, (const void*)nullptr, R, R, a->ld, ctx->vocab,
              ctx->tasks_per_row, ec, partials, counters, (int64_t)0, a->status);
   if (e != hipSuccess) return e;
-  const size_t lds = 2 * (size_t)ctx->tasks_per_row * sizeof(double);
+  const size_t lds =
+      (size_t)(tree_slot_rows(ctx->tasks_per_row) + 1) * (size_t)ctx->tasks_per_row * sizeof(double);
   return launch(tree_point_kernel<DT, VEC>, dim3((unsigned)B), dim3(kThreads), lds, stream, ev, 1,
                 a->target_logits, a->ld, ctx->vocab, R, a->cu_nodes, a->parent, a->tokens,
                 a->uniforms, ec, (const Partial*)partials, ctx->tasks_per_row, L,
@@ -438,6 +440,26 @@ const char* spec_verify_status_string(int status) {
 }
 
 int spec_verify_last_hip_error(void) { return g_last_hip_error; }
+
+int spec_verify_read_probe(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
+                           void* hip_stream, void* start_event, void* stop_event) {
+  if (!src || !sink || bytes == 0 || bytes % sv::kProbeWaveBytes != 0 || !aligned(src, 16) ||
+      !aligned(sink, 4) || (!start_event) != (!stop_event))
+    return SPEC_VERIFY_EINVAL;
+  const int64_t waves = (int64_t)(bytes / sv::kProbeWaveBytes);
+  const int64_t grid = ceil_div(waves, sv::kProbeThreads / 64);
+  if (grid > 0x7fffffffLL) return SPEC_VERIFY_ECAPACITY;
+  hipEvent_t ev[2] = {static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const sv::u32x4* p = static_cast<const sv::u32x4*>(src);
+  const hipError_t e =
+      nontemporal ? launch(sv::read_probe_kernel<true>, dim3((unsigned)grid), dim3(sv::kProbeThreads),
+                           0, s, start_event ? ev : nullptr, 0, p, waves, sink)
+                  : launch(sv::read_probe_kernel<false>, dim3((unsigned)grid),
+                           dim3(sv::kProbeThreads), 0, s, start_event ? ev : nullptr, 0, p, waves,
+                           sink);
+  return e == hipSuccess ? SPEC_VERIFY_OK : hip_fail(e);
+}
 
 // ------------------------------------------------------------------ adaptive draft length
 

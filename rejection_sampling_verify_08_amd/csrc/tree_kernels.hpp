@@ -41,7 +41,6 @@ namespace sv {
 
 constexpr int kMaxTreeNodes = 1024;
 constexpr int kMaxChildren = 64;
-constexpr int kXBatch = 4;        // child-token tasks loaded per round
 
 struct TreeNodes {
   int32_t par[kMaxTreeNodes];
@@ -184,19 +183,45 @@ __global__ __launch_bounds__(kGreedyThreads) void tree_greedy_kernel(
 
 // ---------------------------------------------------------------- point-mass candidates
 
+// Gathered data of up to kSlots internal nodes ("slots"): each node's
+// children (in index order), their distinct tokens in order of first
+// occurrence with the tokens' weights in the node's draw scale, the distinct
+// tasks holding those tokens with the tasks' exact sums without the tokens,
+// the node's task sums, and the node's mass without its children's tokens.
+// A slot's children, tokens and tasks share one range [k0, k0 + nk) of the
+// flat arrays (a node has at least as many children as distinct tokens or
+// tasks).  Small trees gather every internal node in one round of loads;
+// larger trees gather the current node at each level of the walk.
+constexpr int kSlots = 8;            // = kWaves: one wave per slot
+constexpr int64_t kPrefetchNodes = 64;
+constexpr int64_t kPrefetchTasksPerRow = 64;
+constexpr int kPairsPerRound = 1;    // child-token tasks in flight per wave
+static_assert(kSlots == kWaves, "one wave gathers one slot");
+
+// Slots whose task sums the dynamic LDS holds for rows of tpr tasks.
+__host__ __device__ inline int64_t tree_slot_rows(int64_t tpr) {
+  return tpr <= kPrefetchTasksPerRow ? kSlots : 1;
+}
+
 struct TreePointShared {
   TreeNodes tn;
   float M[kMaxTreeNodes];        // row maxima
   double s[kMaxTreeNodes];       // row normalisers (exact scale)
   float lx[kMaxTreeNodes];       // logit of node n's token in its parent's row
   float u[kMaxTreeNodes];        // node n's uniform (root: the final draw)
-  int32_t kids[kMaxChildren];    // children of the current node, in index order
-  int32_t xs[kMaxChildren];      // their distinct tokens
-  float wx[kMaxChildren];        // w of each distinct token in the node's scale
-  int32_t xtask[kMaxChildren];   // distinct tasks holding those tokens
+  int32_t kids[kMaxChildren];    // children, slot by slot
+  int32_t kid_jx[kMaxChildren];  // distinct-token index (in the slot) of each child's token
+  int32_t kid_dup[kMaxChildren]; // the child's token appeared at an earlier child
+  int32_t xs[kMaxChildren];      // distinct child tokens
+  float wx[kMaxChildren];        // their weights in the node's scale
+  int32_t xtask[kMaxChildren];   // distinct tasks holding them
   double xsum[kMaxChildren];     // exact sums of those tasks without the tokens
-  double red[kWaves][kXBatch];   // per-wave partial sums of a batch of tasks
-  int nkids, nx, ntask;
+  int32_t pair[kMaxChildren];    // flat indices of the (slot, task) pairs to load
+  int32_t slot_node[kSlots], slot_k0[kSlots], slot_nk[kSlots], slot_nx[kSlots], slot_nt[kSlots];
+  float slot_Ap[kSlots];
+  double slot_rest[kSlots];      // the node's mass without its children's tokens
+  int nslots, npairs;
+  int prefetch;                  // a small tree: every internal node gathered up front
   int next;                      // accepted child, or -1
   int empty;                     // the final weights summed to 0
 };
@@ -225,6 +250,197 @@ __device__ __forceinline__ void group_weights_without(const GroupRaw<DT>& r, int
   }
 }
 
+// Task sum of a row-pass partial moved into the draw scale 2^(l c + Ap).
+__device__ __forceinline__ double task_sum_in(const Partial& pc, float Ap, const ExpConsts& ec) {
+  return pc.m == -INFINITY ? 0.0 : pc.s * exp2((double)Ap - (double)shift_of(pc.m, ec));
+}
+
+// Gather slots [0, sh.nslots) (slot_node, slot_k0 and slot_nk set): every
+// wave w < nslots lists slot w's children, tokens and tasks; then all waves
+// load the (slot, task) pairs, kPairsPerRound per wave per round, each task
+// as one row-pass wave task (lane l holds groups l, l + 64, ..., l + 448),
+// and the slots' task partials; then wave w sums slot w's mass without its
+// children's tokens.  slot_ts holds kSlots * tpr doubles.  All threads call.
+template <int DT, bool VEC>
+__device__ __forceinline__ void gather_slots(TreePointShared& sh, double* slot_ts,
+                                             const void* target, int64_t ld, int64_t V,
+                                             int64_t g0, int64_t N, const ExpConsts& ec,
+                                             const Partial* __restrict__ part, int64_t tpr) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ns = sh.nslots;
+  if (wave < ns) {
+    const int64_t node = sh.slot_node[wave];
+    const int k0 = sh.slot_k0[wave];
+    const float Ap = shift_of(sh.M[node], ec);
+    int cnt = 0;
+    for (int64_t base = node + 1; base < N; base += 64) {
+      const int64_t n = base + lane;
+      const bool hit = n < N && sh.tn.par[n] == node;
+      const uint64_t m = __ballot(hit);
+      if (hit) sh.kids[k0 + cnt + __builtin_popcountll(m & ((1ull << lane) - 1))] = (int32_t)n;
+      cnt += __builtin_popcountll(m);
+    }
+    // distinct tokens and tasks in order of first occurrence (one child per
+    // lane: a node has at most kMaxChildren = 64 children)
+    const bool act = lane < cnt;
+    const int32_t c = act ? sh.kids[k0 + lane] : 0;
+    const int32_t x = act ? sh.tn.tok[c] : -1;
+    const int32_t t = act ? (int32_t)(x / kWaveTaskElems) : -1;
+    bool first_x = act, first_t = act;
+    int first_lane = lane;
+    for (int j = cnt - 1; j >= 0; --j) {
+      const int32_t xj = __shfl(x, j);
+      if (j < lane && xj == x) {
+        first_x = false;
+        first_lane = j;
+      }
+      if (j < lane && xj / (int32_t)kWaveTaskElems == t) first_t = false;
+    }
+    const uint64_t fx = __ballot(first_x), ft = __ballot(first_t);
+    const uint64_t below = (1ull << lane) - 1;
+    if (first_x) {
+      const int jx = __builtin_popcountll(fx & below);
+      sh.xs[k0 + jx] = x;
+      sh.wx[k0 + jx] = exp_term(sh.lx[c], Ap, ec);
+    }
+    if (first_t) sh.xtask[k0 + __builtin_popcountll(ft & below)] = t;
+    if (act) {
+      sh.kid_jx[k0 + lane] = __builtin_popcountll(fx & ((1ull << first_lane) - 1));
+      sh.kid_dup[k0 + lane] = first_x ? 0 : 1;
+    }
+    if (lane == 0) {
+      sh.slot_nk[wave] = cnt;
+      sh.slot_nx[wave] = __builtin_popcountll(fx);
+      sh.slot_nt[wave] = __builtin_popcountll(ft);
+      sh.slot_Ap[wave] = Ap;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // the (slot, task) pairs: flat index k0 + j for j < nt of each slot
+    int np = 0;
+    for (int sl = 0; sl < ns; ++sl) {
+      const int nt = sh.slot_nt[sl], k0 = sh.slot_k0[sl];
+      if (lane < nt) sh.pair[np + lane] = k0 + lane;
+      np += nt;
+    }
+    if (lane == 0) sh.npairs = np;
+  }
+  __syncthreads();
+  const int np = sh.npairs;
+  // one round of loads: the slots' task partials (at most one per thread:
+  // ns * tpr <= kThreads) and the first kPairsPerRound tasks of every wave
+  // are issued before any of them is used
+  static_assert(kSlots * kPrefetchTasksPerRow <= kThreads, "one slot partial per thread");
+  const bool have_part = tid < (int64_t)ns * tpr;
+  const int my_slot = have_part ? (int)(tid / tpr) : 0;
+  Partial my_part = {-INFINITY, 0.0f, 0.0};
+  if (have_part) my_part = part[(g0 + sh.slot_node[my_slot]) * tpr + (tid - my_slot * tpr)];
+  for (int r0 = wave * kPairsPerRound; r0 < np; r0 += kWaves * kPairsPerRound) {
+    GroupRaw<DT> raw[kPairsPerRound][kTaskGroupsPerLane];
+    int slot_of[kPairsPerRound];
+#pragma unroll
+    for (int q = 0; q < kPairsPerRound; ++q) {
+      slot_of[q] = -1;
+      if (r0 + q < np) {
+        const int f = sh.pair[r0 + q];
+        int sl = 0;
+        while (sl + 1 < ns && sh.slot_k0[sl + 1] <= f) ++sl;
+        slot_of[q] = sl;
+        const void* prow = row_ptr<DT>(target, g0 + sh.slot_node[sl], ld);
+        load_task<DT, VEC>(prow, (int64_t)sh.xtask[f], V, lane, raw[q]);
+      }
+    }
+    if (r0 == wave * kPairsPerRound && have_part)
+      slot_ts[tid] = task_sum_in(my_part, sh.slot_Ap[my_slot], ec);
+#pragma unroll
+    for (int q = 0; q < kPairsPerRound; ++q) {
+      if (slot_of[q] < 0) continue;
+      const int sl = slot_of[q];
+      const int f = sh.pair[r0 + q];
+      const int k0 = sh.slot_k0[sl];
+      const int64_t g_task = (int64_t)sh.xtask[f] * (kWaveTaskElems / kGroup);
+      // bit 8 j + k: logit k of this lane's group j is a child token (the
+      // owning lane of each token sets it)
+      uint64_t excl = 0;
+      const int nx = sh.slot_nx[sl];
+      for (int i = 0; i < nx; ++i) {
+        const int32_t x = sh.xs[k0 + i];
+        const int64_t g = (int64_t)(x / kGroup) - g_task;
+        if (g >= 0 && g < 64 * kTaskGroupsPerLane && (int)(g & 63) == lane)
+          excl |= 1ull << ((g >> 6) * kGroup + (x % kGroup));
+      }
+      const float Ap = sh.slot_Ap[sl];
+      double acc = 0.0;
+#pragma unroll
+      for (int j = 0; j < kTaskGroupsPerLane; ++j) {
+        float v[kGroup], w[kGroup];
+        unpack<DT>(raw[q][j], v);
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k)
+          w[k] = ((excl >> (j * kGroup + k)) & 1) ? 0.0f : exp_term(v[k], Ap, ec);
+        acc += (double)seq_sum8(w);
+      }
+      acc = wave_xor_sum(acc);
+      if (lane == 0) sh.xsum[f] = acc;
+    }
+  }
+  if (wave * kPairsPerRound >= np && have_part)   // no task loads in this wave
+    slot_ts[tid] = task_sum_in(my_part, sh.slot_Ap[my_slot], ec);
+  __syncthreads();
+  if (wave < ns) {
+    // the mass without the children's tokens, in a fixed order
+    const int k0 = sh.slot_k0[wave], nt = sh.slot_nt[wave];
+    const double* ts = slot_ts + (int64_t)wave * tpr;
+    double total = 0.0;
+    for (int64_t c0 = 0; c0 < tpr; c0 += 64) {
+      const int64_t c = c0 + lane;
+      double v = c < tpr ? ts[c] : 0.0;
+      for (int j = 0; j < nt; ++j)
+        if (sh.xtask[k0 + j] == c) v = sh.xsum[k0 + j];
+      total += __shfl(wave_incl_scan(v, lane), 63);
+    }
+    if (lane == 0) sh.slot_rest[wave] = total;
+  }
+  __syncthreads();
+}
+
+// Wave-level tests of the children of `node` (gathered in `slot`), in index
+// order.  Lane i tests child i as if children 0..i-1 were rejected: the first
+// child sees p' = p ([A] 1.2 step 3 with q the point mass at the candidate);
+// a later one sees p without the tokens already rejected -- the slot's
+// distinct tokens 0..d-1 -- p'(x_i) = w(x_i) / (mass without every child
+// token + w_d + ... + w_{nx-1}), summed in that order; a token seen before
+// has p' = 0.  The lowest accepting lane is the child the sequential tests
+// take: lane 0 appends it to the path; every lane returns it, or -1.
+__device__ __forceinline__ int64_t test_children(TreePointShared& sh, int slot, int64_t node,
+                                                 const ExpConsts& ec, int lane) {
+  const int k0 = sh.slot_k0[slot], nk = sh.slot_nk[slot], nx = sh.slot_nx[slot];
+  bool accept = false;
+  if (lane < nk) {
+    const int32_t c = sh.kids[k0 + lane];
+    const int jx = sh.kid_jx[k0 + lane];
+    double r;
+    if (lane == 0) {
+      r = exp(((double)sh.lx[c] - (double)sh.M[node]) / ec.T) / sh.s[node];
+    } else if (sh.kid_dup[k0 + lane]) {
+      r = 0.0;
+    } else {
+      double rest = sh.slot_rest[slot];
+      for (int j = jx; j < nx; ++j) rest += (double)sh.wx[k0 + j];
+      r = rest > 0.0 ? (double)sh.wx[k0 + jx] / rest : 0.0;
+    }
+    accept = (double)sh.u[c] < r;
+  }
+  const uint64_t acc = __ballot(accept);
+  if (!acc) return -1;
+  const int64_t next = sh.kids[k0 + __builtin_ctzll(acc)];
+  if (lane == 0) sh.tn.path[sh.tn.depth++] = (int32_t)next;
+  return next;
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void tree_point_kernel(
     const void* __restrict__ target, int64_t ld, int64_t V, int64_t R,
@@ -235,9 +451,11 @@ __global__ __launch_bounds__(kThreads) void tree_point_kernel(
     int32_t* __restrict__ out_num_accepted, uint32_t* __restrict__ status) {
   __shared__ TreePointShared sh;
   __shared__ DrawShared ds;
-  extern __shared__ double lds_dyn[];   // [2 * tpr]: converted task sums, draw sums
-  double* task_sum = lds_dyn;
-  double* draw_sum = lds_dyn + tpr;
+  // dynamic LDS: the slots' task sums (kSlots slots when the row has at most
+  // kPrefetchTasksPerRow tasks, else one), then the draw sums
+  extern __shared__ double lds_dyn[];
+  double* slot_ts = lds_dyn;
+  double* draw_sum = lds_dyn + tree_slot_rows(tpr) * tpr;
   constexpr int64_t kTaskGroups = kWaveTaskElems / kGroup;   // 512 = one group per thread
   static_assert(kTaskGroups == kThreads, "a task is one group per thread");
   const int tid = threadIdx.x;
@@ -306,154 +524,126 @@ __global__ __launch_bounds__(kThreads) void tree_point_kernel(
       }
     }
   }
-  if (tid == 0) sh.tn.depth = 0;
+  // ---- small trees (at most kPrefetchNodes nodes and kSlots internal nodes,
+  // rows of at most kPrefetchTasksPerRow tasks): every internal node is
+  // gathered now, in one round of loads, and wave 0 walks without loads.
+  // Larger trees gather the current node at each level of the walk.
+  if (wave == 0) {
+    int ns = 0, k0 = 0;
+    bool fits = N <= kPrefetchNodes && tpr <= kPrefetchTasksPerRow;
+    for (int64_t base = 0; fits && base < N; base += 64) {
+      const int64_t n = base + lane;
+      const int nk = n < N ? sh.tn.nkids[n] : 0;
+      const uint64_t m = __ballot(nk > 0);
+      if (ns + __builtin_popcountll(m) > kSlots) {
+        fits = false;
+        break;
+      }
+      // flat ranges in node order
+      int before = nk;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(before, o);
+        if (lane >= o) before += t;
+      }
+      if (nk > 0) {
+        const int sl = ns + __builtin_popcountll(m & ((1ull << lane) - 1));
+        sh.slot_node[sl] = (int32_t)n;
+        sh.slot_k0[sl] = k0 + before - nk;
+      }
+      ns += __builtin_popcountll(m);
+      k0 += __shfl(before, 63);
+    }
+    if (lane == 0) {
+      sh.prefetch = fits ? 1 : 0;
+      sh.nslots = fits ? ns : 0;
+      sh.tn.depth = 0;
+    }
+  }
   __syncthreads();
 
-  // The groups of the last batch of child-token tasks stay in registers: the
-  // final search reuses them when it lands in one of those tasks.
-  GroupRaw<DT> xraw[kXBatch];
-  int32_t xraw_task[kXBatch];
-#pragma unroll
-  for (int j = 0; j < kXBatch; ++j) xraw_task[j] = -1;
-  uint32_t fbad = 0;
+  // ---- the walk from the root
   int64_t cur = 0;
-  for (;;) {
-    const void* prow = row_ptr<DT>(target, g0 + cur, ld);
-    const float Ap = shift_of(sh.M[cur], ec);
-    // ---- the current node's children in index order, their distinct tokens
-    // and the tasks holding them (wave 0)
+  int slot = -1;
+  if (sh.prefetch) {
+    if (sh.nslots > 0) gather_slots<DT, VEC>(sh, slot_ts, target, ld, V, g0, N, ec, part, tpr);
     if (wave == 0) {
-      int cnt = 0;
-      for (int64_t base = cur + 1; base < N; base += 64) {
-        const int64_t n = base + lane;
-        const bool hit = n < N && sh.tn.par[n] == cur;
-        const uint64_t m = __ballot(hit);
-        if (hit) sh.kids[cnt + __builtin_popcountll(m & ((1ull << lane) - 1))] = (int32_t)n;
-        cnt += __builtin_popcountll(m);
+      int64_t c = 0;
+      int sl = -1;
+      for (;;) {
+        sl = -1;
+        for (int k = 0; k < sh.nslots; ++k)
+          if (sh.slot_node[k] == c) sl = k;
+        if (sl < 0) break;
+        const int64_t nxt = test_children(sh, sl, c, ec, lane);
+        if (nxt < 0) break;
+        c = nxt;
       }
       if (lane == 0) {
-        int nx = 0, nt = 0;
-        for (int i = 0; i < cnt; ++i) {
-          const int32_t c = sh.kids[i];
-          const int32_t x = sh.tn.tok[c];
-          bool seen = false;
-          for (int j = 0; j < nx; ++j) seen = seen || sh.xs[j] == x;
-          if (seen) continue;
-          sh.xs[nx] = x;
-          sh.wx[nx] = exp_term(sh.lx[c], Ap, ec);
-          ++nx;
-          const int32_t t = (int32_t)(x / kWaveTaskElems);
-          bool tseen = false;
-          for (int j = 0; j < nt; ++j) tseen = tseen || sh.xtask[j] == t;
-          if (!tseen) sh.xtask[nt++] = t;
-        }
-        sh.nkids = cnt;
-        sh.nx = nx;
-        sh.ntask = nt;
-        sh.next = -1;
+        sh.next = (int32_t)c;   // the node of the final draw
+        sh.empty = sl;          // its slot (-1: no children)
       }
     }
     __syncthreads();
-    const int nk = sh.nkids, nx = sh.nx, ntask = sh.ntask;
-    // ---- one round of loads: the row's task partials and the groups of the
-    // tasks holding child tokens; then the task sums in the draw's scale
-    // 2^(l c + Ap) and those tasks summed without the child tokens
-    const Partial* prt = part + (g0 + cur) * tpr;
-    for (int64_t j0 = 0; j0 < (ntask > 0 ? ntask : 1); j0 += kXBatch) {
-      const int nb = ntask - (int)j0 < kXBatch ? ntask - (int)j0 : kXBatch;
-#pragma unroll
-      for (int j = 0; j < kXBatch; ++j) {
-        xraw_task[j] = j < nb ? sh.xtask[j0 + j] : -1;
-        if (j < nb) load_group<DT, VEC>(prow, (int64_t)xraw_task[j] * kTaskGroups + tid, V, xraw[j]);
+    cur = sh.next;
+    slot = sh.empty;
+    __syncthreads();            // sh.next and sh.empty are reused below
+  } else {
+    for (;;) {
+      if (sh.tn.nkids[cur] == 0) {
+        slot = -1;              // a node without children: the final draw from p
+        break;
       }
-      if (j0 == 0)
-        for (int64_t c = tid; c < tpr; c += kThreads) {
-          const Partial pc = prt[c];
-          task_sum[c] = pc.m == -INFINITY ? 0.0
-                                          : pc.s * exp2((double)Ap - (double)shift_of(pc.m, ec));
-        }
-#pragma unroll
-      for (int j = 0; j < kXBatch; ++j) {
-        double gs = 0.0;
-        if (j < nb) {
-          float w[kGroup];
-          group_weights_without<DT>(xraw[j], (int64_t)xraw_task[j] * kTaskGroups + tid, Ap, ec,
-                                    sh.xs, nx, w);
-          gs = (double)seq_sum8(w);
-        }
-        gs = __shfl(wave_incl_scan(gs, lane), 63);
-        if (lane == 0) sh.red[wave][j] = gs;
+      __syncthreads();          // the previous level's slot is read no more
+      if (tid == 0) {
+        sh.nslots = 1;
+        sh.slot_node[0] = (int32_t)cur;
+        sh.slot_k0[0] = 0;
       }
       __syncthreads();
-      if (tid < nb) {
-        double t = 0.0;
-        for (int v = 0; v < kWaves; ++v) t += sh.red[v][tid];
-        sh.xsum[j0 + tid] = t;
+      gather_slots<DT, VEC>(sh, slot_ts, target, ld, V, g0, N, ec, part, tpr);
+      slot = 0;
+      if (wave == 0) {
+        const int64_t nxt = test_children(sh, 0, cur, ec, lane);
+        if (lane == 0) sh.next = (int32_t)nxt;
       }
       __syncthreads();
+      const int64_t nxt = sh.next;
+      if (nxt < 0) break;       // every child rejected: the final draw at cur
+      cur = nxt;
     }
-    // ---- wave 0: the mass without the children's tokens, then the tests
-    // in index order.  The first child sees p' = p ([A] 1.2 step 3 with q
-    // the point mass at the candidate); each later one p without the tokens
-    // already rejected: p'(x) = w(x) / (mass without every child token + the
-    // child tokens not yet rejected).
-    if (wave == 0 && nk > 0) {
-      for (int64_t c = lane; c < tpr; c += 64) {
-        double v = task_sum[c];
-        for (int j = 0; j < ntask; ++j)
-          if (sh.xtask[j] == c) v = sh.xsum[j];
-        draw_sum[c] = v;
-      }
-      const double rest_x = wave_total(draw_sum, tpr, lane);
-      if (lane == 0) {
-        uint64_t removed = 0;   // bit j: xs[j] rejected
-        for (int i = 0; i < nk; ++i) {
-          const int32_t c = sh.kids[i];
-          const int32_t x = sh.tn.tok[c];
-          int jx = 0;
-          while (sh.xs[jx] != x) ++jx;
-          double r;
-          if (i == 0) {
-            r = exp(((double)sh.lx[c] - (double)sh.M[cur]) / ec.T) / sh.s[cur];
-          } else if ((removed >> jx) & 1) {
-            r = 0.0;
-          } else {
-            double rest = rest_x;
-            for (int j = 0; j < nx; ++j)
-              if (!((removed >> j) & 1)) rest += (double)sh.wx[j];
-            r = rest > 0.0 ? (double)sh.wx[jx] / rest : 0.0;
-          }
-          if ((double)sh.u[c] < r) {
-            sh.next = c;
-            break;
-          }
-          removed |= 1ull << jx;
-        }
-      }
-    }
-    __syncthreads();
-    if (sh.next >= 0) {
-      if (tid == 0) sh.tn.path[sh.tn.depth++] = sh.next;
-      cur = sh.next;
-      __syncthreads();
-      continue;
-    }
-    break;
   }
 
   // ---- final draw at `cur`: from p without its children's tokens (every
   // child was rejected), or from p at a node without children
-  const int nk = sh.nkids;
   const void* prow = row_ptr<DT>(target, g0 + cur, ld);
   const float Ap = shift_of(sh.M[cur], ec);
+  uint32_t fbad = 0;
+  if (slot < 0) {
+    // p at a node without children: its task sums
+    for (int64_t c = tid; c < tpr; c += kThreads)
+      draw_sum[c] = task_sum_in(part[(g0 + cur) * tpr + c], Ap, ec);
+    __syncthreads();
+  }
+  const int k0 = slot >= 0 ? sh.slot_k0[slot] : 0;
+  const int nt = slot >= 0 ? sh.slot_nt[slot] : 0;
+  const int nx = slot >= 0 ? sh.slot_nx[slot] : 0;
   if (wave == 0) {
-    const double* sums = nk > 0 ? draw_sum : task_sum;
+    const double* ts = slot >= 0 ? slot_ts + (int64_t)slot * tpr : draw_sum;
+    if (slot >= 0) {
+      for (int64_t c = lane; c < tpr; c += 64) {
+        double v = ts[c];
+        for (int j = 0; j < nt; ++j)
+          if (sh.xtask[k0 + j] == c) v = sh.xsum[k0 + j];
+        draw_sum[c] = v;
+      }
+    }
+    const double* sums = draw_sum;
     double total = wave_total(sums, tpr, lane);
     int empty = 0;
     if (!(total > 0.0)) {
       // empty residual (invalid input or extreme rounding): draw from p
       empty = 1;
-      sums = task_sum;
+      sums = ts;
       total = wave_total(sums, tpr, lane);
     }
     const double tt = (double)sh.u[0] * total;
@@ -464,23 +654,16 @@ __global__ __launch_bounds__(kThreads) void tree_point_kernel(
     }
   }
   __syncthreads();
-  const bool exclude = nk > 0 && !sh.empty;
+  const bool exclude = slot >= 0 && !sh.empty;
   if (sh.empty) fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
   const int64_t tau = ds.tau;
   int64_t token = -1;
   if (tau >= 0) {
     GroupRaw<DT> r;
-    bool have = false;
-#pragma unroll
-    for (int j = 0; j < kXBatch; ++j)
-      if (xraw_task[j] == tau) {
-        r = xraw[j];
-        have = true;
-      }
     const int64_t gi = tau * kTaskGroups + tid;
-    if (!have) load_group<DT, VEC>(prow, gi, V, r);
+    load_group<DT, VEC>(prow, gi, V, r);
     float w[kGroup];
-    group_weights_without<DT>(r, gi, Ap, ec, sh.xs, exclude ? sh.nx : 0, w);
+    group_weights_without<DT>(r, gi, Ap, ec, sh.xs + k0, exclude ? nx : 0, w);
     const double tt = ds.tt, p_excl = ds.p_excl;
     __syncthreads();   // ds is reused by the search
     token = block_search_weights(w, gi, tt, p_excl, ds);

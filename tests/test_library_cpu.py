@@ -128,6 +128,15 @@ def test_host_side_argument_checks_without_a_device():
     assert lib.spec_verify_destroy(None) == binding.OK
     assert lib.spec_verify_workspace_size(None) == 0
     assert lib.spec_verify_num_kernels(None) == 0
+    # the read probe: null pointers, sizes that are not whole 8 KB wave spans,
+    # misalignment and half an event pair are refused on the host
+    P = ctypes.c_void_p
+    assert lib.spec_verify_read_probe(None, 8192, 1, P(256), None, None, None) == binding.EINVAL
+    assert lib.spec_verify_read_probe(P(256), 8192, 1, None, None, None, None) == binding.EINVAL
+    assert lib.spec_verify_read_probe(P(256), 0, 1, P(256), None, None, None) == binding.EINVAL
+    assert lib.spec_verify_read_probe(P(256), 8000, 1, P(256), None, None, None) == binding.EINVAL
+    assert lib.spec_verify_read_probe(P(264), 8192, 1, P(256), None, None, None) == binding.EINVAL
+    assert lib.spec_verify_read_probe(P(256), 8192, 1, P(256), None, P(8), None) == binding.EINVAL
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):

@@ -88,6 +88,16 @@ def test_tree_shapes_and_vocab(mode, dtype, V):
     _check(tr, mode, f"mixed shapes V={V} {dtype}")
 
 
+@pytest.mark.parametrize("mode", ["greedy", "point"])
+def test_tree_rows_of_more_than_64_tasks(mode):
+    # V = 300000: 74 row-pass tasks per row, so even small trees gather the
+    # current node at each level instead of every internal node at once
+    tr = W.build_tree("wide rows", 77, [W.tree_shape(W.TREE_17)] * 4 +
+                      [W.tree_shape([(1, 1)] * 12), W.tree_shape([(1, 5), (5, 2)])], 300000,
+                      W.BF16, 1.0, W.boosted_top_rows(2.0, 4, 6.0), 0.6)
+    _check(tr, mode, "V=300000")
+
+
 @pytest.mark.parametrize("T", [0.7, 1.0, 1.3])
 def test_tree_point_temperatures(T):
     tr = W.build_tree("temps", 51, [W.tree_shape(W.TREE_17)] * 24, 32000, W.BF16, T,
