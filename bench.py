@@ -96,8 +96,17 @@ def cpu_baseline(inp, budget_s: float):
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 50:
             break
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": inp.target_rows * runs / el, "unit": "verified rows/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": model, "host_nproc": os.cpu_count(),
             "sample": f"the full headline batch ({inp.num_seqs} sequences, {inp.target_rows} "
                       f"target rows), {runs} run(s) in {el:.1f} s, single-threaded float64 C"}
 
@@ -395,6 +404,8 @@ def main() -> int:
                    "V": inp.vocab, "logits": inp.dtype, "temperature": inp.temperature,
                    "accumulate": "f64", "input_sets": len(sets),
                    "target_rows": inp.target_rows, "draft_rows": inp.draft_rows},
+        "sequences_per_s": round(inp.num_seqs / (ms_step / 1e3), 1),
+        "all_rows_per_s": round((inp.target_rows + inp.draft_rows) / (ms_step / 1e3), 1),
         "hbm_gbps": round(hbm, 1), "hbm_frac": round(hbm / PEAK_HBM_GBPS, 4),
         "step_algorithmic_bytes": step_bytes,
         "kernel_avg_us": [round(x * 1e3, 2) for x in k_avg],
