@@ -261,6 +261,46 @@ def test_modes_share_one_context_and_workspace():
         np.testing.assert_array_equal(got.num_accepted, ref[m].num_accepted, err_msg=m)
 
 
+def test_concurrent_streams_with_separate_workspaces():
+    """One context, two workspaces, calls on two streams that overlap (the
+    header allows it): every result equals the same call made alone."""
+    import torch
+    from rejection_sampling_verify_08_amd import SpecVerifier
+    inps = [W.config(2, seed=300 + k, num_seqs=48) for k in range(2)]
+    dets = [W.with_deterministic_drafts(x) for x in inps]
+    refs = [(run_gpu(inps[k]), run_gpu(dets[k], mode="point"), run_gpu(dets[k], mode="greedy"))
+            for k in range(2)]
+    sv = SpecVerifier(inps[0].vocab, inps[0].dtype, max_seqs=48,
+                      max_draft_rows=max(x.draft_rows for x in inps))
+    # a second workspace for the same context
+    ws2 = torch.empty_like(sv.workspace)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    devs = [to_device(inps[k]) for k in range(2)]
+    toks = [torch.from_numpy(dets[k].draft_tokens).cuda() for k in range(2)]
+    outs = [[sv.allocate_outputs(48, inps[k].draft_rows) for _ in range(3)] for k in range(2)]
+    torch.cuda.synchronize()
+    ws1 = sv.workspace
+    for rep in range(3):
+        for k in range(2):
+            sv.workspace = ws1 if k == 0 else ws2
+            d = devs[k]
+            with torch.cuda.stream(streams[k]):
+                sv(d.cu, d.target, d.draft, d.tokens, d.uniforms, inps[k].temperature,
+                   out=outs[k][0], stream=streams[k])
+                sv.point_drafts(d.cu, d.target, toks[k], d.uniforms, inps[k].temperature,
+                                out=outs[k][1], stream=streams[k])
+                sv.greedy(d.cu, d.target, toks[k], out=outs[k][2], stream=streams[k])
+        sv.workspace = ws1
+        torch.cuda.synchronize()
+        for k in range(2):
+            for j in range(3):
+                got, ref = outs[k][j], refs[k][j]
+                np.testing.assert_array_equal(got.out_tokens.cpu().numpy(), ref.out_tokens,
+                                              err_msg=f"rep {rep} stream {k} call {j}")
+                np.testing.assert_array_equal(got.num_accepted.cpu().numpy(), ref.num_accepted,
+                                              err_msg=f"rep {rep} stream {k} call {j}")
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_configurations_greedy_and_point(seed):
     rng = np.random.default_rng(30_000 + seed)
