@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -43,9 +44,12 @@ KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_08_amd", "csrc",
 
 
 def kernel_source_hash() -> str:
+    """Identity of the kernel code: a hash of the kernel sources with comments
+    and blank lines removed (an edit to a comment leaves it unchanged)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+        src = re.sub(r"//[^\n]*", "", open(f).read())
+        h.update("\n".join(l.rstrip() for l in src.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -29,12 +29,13 @@
 // Both kernels run after a row pass over the R node rows (argmax_kernel or
 // row_stats_kernel) and use one workgroup per sequence: the tree's nodes go
 // to LDS, every row's statistic is combined at once, then one wave walks the
-// tree from the root.  The point kernel computes, when a node's first child
-// is rejected, the exact mass of the node's row without its children's
-// tokens: the row pass's task sums moved into one scale, and the tasks that
-// hold a child token summed again without those tokens (never by
-// subtraction).  Every later sibling's renormalised probability, and the
-// final draw, use those sums.
+// tree from the root.  The point kernel needs, at a node whose children are
+// tested, the exact mass of the node's row without its children's tokens:
+// the row pass's task sums moved into one scale, and the tasks that hold a
+// child token summed again without those tokens (never by subtraction).
+// Every sibling after the first, and the final draw, use those sums.  Small
+// trees gather them for every internal node in one round of loads before the
+// walk; larger trees gather the current node at each level.
 #pragma once
 
 namespace sv {
