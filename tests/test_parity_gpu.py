@@ -56,6 +56,17 @@ def test_temperatures(T):
     _check(inp, f"T={T}")
 
 
+@pytest.mark.parametrize("T", [0.05, 0.2, 5.0, 20.0])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_extreme_temperatures(T, dtype):
+    """Near-one-hot (small T) and near-flat (large T) distributions: the
+    exponent range, the two-float temperature constant and the residual's
+    scale factor at their extremes."""
+    inp = W.build(f"T{T} {dtype}", 56, [4, 8, 0, 3, 8, 1, 6, 2], 50000, dtype, T,
+                  W.iid_normal_rows(3.0), 0.4)
+    _check(inp, f"T={T} {dtype}")
+
+
 def test_ragged_batch_with_long_drafts():
     """gamma up to 70 (more than one 64-lane ballot window) mixed with 0."""
     gam = [70, 0, 3, 65, 64, 0, 1, 63]

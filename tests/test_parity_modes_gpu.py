@@ -166,7 +166,7 @@ def test_point_vocab_sizes(V, dtype):
     _point(inp, f"V={V} {dtype}")
 
 
-@pytest.mark.parametrize("T", [0.7, 0.8, 1.0, 1.3])
+@pytest.mark.parametrize("T", [0.05, 0.2, 0.7, 0.8, 1.0, 1.3, 5.0, 20.0])
 def test_point_temperatures(T):
     inp = W.build(f"pT{T}", 56, [2, 6, 0, 8, 5, 1], 32000, W.BF16, T,
                   W.boosted_random_ids_rows(3.0, 20, 8.0), 1.0)

@@ -98,7 +98,7 @@ def test_tree_rows_of_more_than_64_tasks(mode):
     _check(tr, mode, "V=300000")
 
 
-@pytest.mark.parametrize("T", [0.7, 1.0, 1.3])
+@pytest.mark.parametrize("T", [0.05, 0.2, 0.7, 1.0, 1.3, 5.0, 20.0])
 def test_tree_point_temperatures(T):
     tr = W.build_tree("temps", 51, [W.tree_shape(W.TREE_17)] * 24, 32000, W.BF16, T,
                       W.boosted_random_ids_rows(3.0, 20, 8.0), 1.0)
