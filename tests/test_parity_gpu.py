@@ -67,6 +67,21 @@ def test_extreme_temperatures(T, dtype):
     _check(inp, f"T={T} {dtype}")
 
 
+@pytest.mark.parametrize("kind", ["uniform", "large_constant", "huge_spread"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_degenerate_rows(kind, dtype):
+    """Uniform rows with draft = target (every draft accepted, bonus from a
+    flat p), rows of one large constant, and logits with a standard
+    deviation of 1000 (every row effectively one-hot)."""
+    rows = {"uniform": lambda rng, brng, V: np.zeros(V),
+            "large_constant": lambda rng, brng, V: np.full(V, 3000.0),
+            "huge_spread": lambda rng, brng, V: rng.standard_normal(V) * 1000.0}[kind]
+    sd = 300.0 if kind == "huge_spread" else 0.0
+    inp = W.build(f"degenerate {kind} {dtype}", 58, [5, 0, 8, 2, 7, 1], 40000, dtype, 1.0,
+                  rows, sd)
+    _check(inp, f"{kind} {dtype}")
+
+
 def test_ragged_batch_with_long_drafts():
     """gamma up to 70 (more than one 64-lane ballot window) mixed with 0."""
     gam = [70, 0, 3, 65, 64, 0, 1, 63]
