@@ -82,6 +82,16 @@ def test_degenerate_rows(kind, dtype):
     _check(inp, f"{kind} {dtype}")
 
 
+@pytest.mark.parametrize("V", [300000, 1 << 21])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_largest_vocabularies(V, dtype):
+    """More than 64 row-pass partials per row (the combine's looping path) and
+    V = 2^21, the largest supported vocabulary (1024 tiles of tile sums)."""
+    inp = W.build(f"V{V} {dtype}", 59, [3, 0, 5, 2, 8], V, dtype, 1.0,
+                  W.boosted_random_ids_rows(2.0, 30, 7.0), 0.8)
+    _check(inp, f"V={V} {dtype}")
+
+
 def test_ragged_batch_with_long_drafts():
     """gamma up to 70 (more than one 64-lane ballot window) mixed with 0."""
     gam = [70, 0, 3, 65, 64, 0, 1, 63]

@@ -261,6 +261,17 @@ def test_modes_share_one_context_and_workspace():
         np.testing.assert_array_equal(got.num_accepted, ref[m].num_accepted, err_msg=m)
 
 
+@pytest.mark.parametrize("V", [300000, 1 << 21])
+def test_greedy_and_point_largest_vocabularies(V):
+    inp = W.with_deterministic_drafts(W.build(f"modes V{V}", 61, [3, 0, 5, 2, 8], V, W.BF16,
+                                              1.0, W.boosted_random_ids_rows(2.0, 30, 7.0), 0.8))
+    g = run_gpu(inp, mode="greedy")
+    og = oracle_greedy(inp)
+    np.testing.assert_array_equal(g.out_tokens, og.out_tokens)
+    np.testing.assert_array_equal(g.num_accepted, og.num_accepted)
+    _point(inp, f"V={V}")
+
+
 def test_concurrent_streams_with_separate_workspaces():
     """One context, two workspaces, calls on two streams that overlap (the
     header allows it): every result equals the same call made alone."""

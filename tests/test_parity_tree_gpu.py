@@ -98,6 +98,14 @@ def test_tree_rows_of_more_than_64_tasks(mode):
     _check(tr, mode, "V=300000")
 
 
+@pytest.mark.parametrize("mode", ["greedy", "point"])
+def test_tree_largest_vocabulary(mode):
+    tr = W.build_tree("V 2^21", 79, [W.tree_shape(W.TREE_17), W.tree_shape([(1, 3), (3, 2)]),
+                                     np.asarray([-1], np.int32)], 1 << 21, W.BF16, 1.0,
+                      W.boosted_top_rows(2.0, 4, 6.0), 0.6)
+    _check(tr, mode, "V=2^21")
+
+
 @pytest.mark.parametrize("T", [0.05, 0.2, 0.7, 1.0, 1.3, 5.0, 20.0])
 def test_tree_point_temperatures(T):
     tr = W.build_tree("temps", 51, [W.tree_shape(W.TREE_17)] * 24, 32000, W.BF16, T,
