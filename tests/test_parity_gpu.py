@@ -92,6 +92,15 @@ def test_largest_vocabularies(V, dtype):
     _check(inp, f"V={V} {dtype}")
 
 
+def test_many_short_sequences():
+    """Thousands of sequences (one finishing workgroup each) with gamma in
+    0..4 over a small vocabulary."""
+    rng = np.random.default_rng(60)
+    inp = W.build("many seqs", 60, rng.integers(0, 5, size=3000), 1000, W.F32, 0.9,
+                  W.iid_normal_rows(2.0), 0.5)
+    _check(inp, "B=3000 V=1000")
+
+
 def test_ragged_batch_with_long_drafts():
     """gamma up to 70 (more than one 64-lane ballot window) mixed with 0."""
     gam = [70, 0, 3, 65, 64, 0, 1, 63]

@@ -99,6 +99,15 @@ def test_tree_rows_of_more_than_64_tasks(mode):
 
 
 @pytest.mark.parametrize("mode", ["greedy", "point"])
+def test_many_small_trees(mode):
+    shapes = [W.tree_shape(W.TREE_17), W.tree_shape([(1, 2)]), np.asarray([-1], np.int32),
+              W.tree_shape([(1, 1)] * 3)] * 500
+    tr = W.build_tree("many trees", 81, shapes, 2000, W.F32, 1.0,
+                      W.boosted_top_rows(1.5, 4, 5.0), 0.6)
+    _check(tr, mode, "B=2000 trees")
+
+
+@pytest.mark.parametrize("mode", ["greedy", "point"])
 def test_tree_largest_vocabulary(mode):
     tr = W.build_tree("V 2^21", 79, [W.tree_shape(W.TREE_17), W.tree_shape([(1, 3), (3, 2)]),
                                      np.asarray([-1], np.int32)], 1 << 21, W.BF16, 1.0,
