@@ -782,11 +782,17 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     auto table_row = [&](int64_t r) -> int64_t {
       return r < nt ? prow_t0 + lo + r : prow_d0 + lo + (r - nt);
     };
-    const int64_t stride = (int64_t)kWaves * rows_per_wave;
-    if (tpr <= L) {
+    // waves 1..7 combine (wave 0's loads wait on the draft tokens, so it
+    // would join the combine late)
+    const int cwave = wave - 1;
+    const int64_t stride = (int64_t)(kWaves - 1) * rows_per_wave;
+    if (wave == 0) {
+      // the tokens, uniforms and logits above
+    } else if (tpr <= L) {
       // one partial per lane; two passes' loads are issued before either
-      // is reduced (a 64-position window with gamma up to 16 needs two)
-      for (int64_t r0 = (int64_t)wave * rows_per_wave; r0 < nt + nd; r0 += 2 * stride) {
+      // is reduced (with 32 lanes per row one iteration covers 28 rows,
+      // gamma up to 13)
+      for (int64_t r0 = (int64_t)cwave * rows_per_wave; r0 < nt + nd; r0 += 2 * stride) {
         const int64_t ra = r0 + lane / L, rb = ra + stride;
         const bool act_a = (lane / L) < rows_per_wave && ra < nt + nd;
         const bool act_b = (lane / L) < rows_per_wave && rb < nt + nd;
@@ -796,7 +802,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
         store_row(rb, act_b, reduce_partials(pb, L, ec));
       }
     } else {
-      for (int64_t r0 = (int64_t)wave * rows_per_wave; r0 < nt + nd; r0 += stride) {
+      for (int64_t r0 = (int64_t)cwave * rows_per_wave; r0 < nt + nd; r0 += stride) {
         const int64_t r = r0 + lane / L;
         const bool active = (lane / L) < rows_per_wave && r < nt + nd;
         store_row(r, active, combine_rows_packed(part, tpr, L, active ? table_row(r) : 0,
