@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "spec_verify_kernels.hpp"   // the wave-level steps
+
 namespace sv {
 
 struct AdaptLayout {
@@ -205,18 +207,10 @@ __global__ __launch_bounds__(kAdaptThreads) void adapt_update_kernel(
       }
     }
     // inclusive wave scan of k, then wave totals through LDS
-    int64_t incl = k;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      v += __shfl_xor(v, o);
-      a += __shfl_xor(a, o);
-      d += __shfl_xor(d, o);
-    }
+    const int64_t incl = sv::wave_scan(k);
+    v = sv::group_reduce(v, 64, sv::OpAdd());
+    a = sv::group_reduce(a, 64, sv::OpAdd());
+    d = sv::group_reduce(d, 64, sv::OpAdd());
     if (lane == 63) wave_k[wave] = incl;
     if (lane == 0) {
       wave_stat[0][wave] = v;
@@ -239,8 +233,7 @@ __global__ __launch_bounds__(kAdaptThreads) void adapt_update_kernel(
     __syncthreads();   // wave_k / wave_stat are reused by the next chunk
   }
   // any thread's bad bits reach the status word
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
+  bad = sv::wave_or(bad);
   if (lane == 0 && bad && status) atomicOr(status, bad);
   if (tid == 0) {
     if (next_cu) next_cu[B] = (int32_t)carry;

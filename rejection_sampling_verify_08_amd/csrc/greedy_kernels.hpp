@@ -39,17 +39,45 @@ __device__ __forceinline__ bool arg_better(float v, int64_t k, float bv, int64_t
   return v > bv || (v == bv && k < bk);
 }
 
-__device__ __forceinline__ void wave_argmax(float& v, int64_t& k) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o);
-    const int64_t ok = __shfl_xor(k, o);
+// Butterfly over groups of `width` consecutive lanes (a power of two <= 64,
+// wave-uniform), in the same lane steps as group_reduce: every lane of a
+// group ends with the group's best (v, k).  The order is strict on the
+// values that occur (no NaN ever becomes a candidate), so both lanes of a
+// pair pick the same winner.
+__device__ __forceinline__ void group_argmax(float& v, int64_t& k, int width) {
+  using LF = LaneBits<float>;
+  using LK = LaneBits<int64_t>;
+  auto step = [&](float ov, int64_t ok) {
     if (arg_better(ov, ok, v, k)) {
       v = ov;
       k = ok;
     }
+  };
+  if (width > 1) step(LF::dpp<kDppQuadXor1>(v), LK::dpp<kDppQuadXor1>(k));
+  if (width > 2) step(LF::dpp<kDppQuadXor2>(v), LK::dpp<kDppQuadXor2>(k));
+  if (width > 4) step(LF::dpp<kDppHalfMirror>(v), LK::dpp<kDppHalfMirror>(k));
+  if (width > 8) step(LF::dpp<kDppMirror>(v), LK::dpp<kDppMirror>(k));
+  if (width > 16) {
+    float av, bv;
+    int64_t ak, bk;
+    LF::swap16(v, av, bv);
+    LK::swap16(k, ak, bk);
+    v = av;
+    k = ak;
+    step(bv, bk);
+  }
+  if (width > 32) {
+    float av, bv;
+    int64_t ak, bk;
+    LF::swap32(v, av, bv);
+    LK::swap32(k, ak, bk);
+    v = av;
+    k = ak;
+    step(bv, bk);
   }
 }
+
+__device__ __forceinline__ void wave_argmax(float& v, int64_t& k) { group_argmax(v, k, 64); }
 
 // Wave task t covers target row t / tasks_per_row, logits
 // [(t % tasks_per_row) * 4096, +4096); partial index = t.
@@ -113,14 +141,7 @@ __device__ __forceinline__ int64_t combine_argmax(const ArgPartial* __restrict__
         bk = p.k;
       }
     }
-  for (int o = L >> 1; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int64_t ok = __shfl_xor(bk, o);
-    if (arg_better(ov, ok, bv, bk)) {
-      bv = ov;
-      bk = ok;
-    }
-  }
+  group_argmax(bv, bk, L);
   return bk;
 }
 

@@ -111,33 +111,179 @@ __device__ __forceinline__ double offset_of(float m, float A, const ExpConsts& c
   return ((double)A + (double)m * (double)c.c_hi) + (double)m * (double)c.c_lo;
 }
 
+// ---- cross-lane steps without the LDS crossbar.  A butterfly over 64 lanes
+// runs in rising distance: lanes 1 and 2 apart through quad permutations,
+// then 4 and 8 through the half-row and row mirrors (after the first two
+// steps a quad holds one value in all four lanes, so the mirror partner
+// holds what the xor partner holds), then 16 and 32 through the permlane
+// swaps (each gives every lane the even and the odd half, in that order).
+// Each step combines the same two operands in every lane, so all lanes end
+// with bitwise equal results.
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  // lanes whose source is outside the row, or whose row is masked, get 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within 16
+constexpr int kDppRowShr = 0x110;     // + n: lane i <- i - n within a row of 16
+constexpr int kDppBcast15 = 0x142;    // lane 15 of a row -> the next row
+constexpr int kDppBcast31 = 0x143;    // lane 31 -> rows 2 and 3
+
+template <typename T>
+struct LaneBits;
+template <>
+struct LaneBits<float> {
+  template <int CTRL, int RM = 0xF>
+  __device__ static float dpp(float v) { return __uint_as_float(dpp_u32<CTRL, RM>(__float_as_uint(v))); }
+  __device__ static void swap16(float v, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+  __device__ static void swap32(float v, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+  __device__ static float read(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+  }
+};
+template <>
+struct LaneBits<uint32_t> {
+  template <int CTRL, int RM = 0xF>
+  __device__ static uint32_t dpp(uint32_t v) { return dpp_u32<CTRL, RM>(v); }
+  __device__ static void swap16(uint32_t v, uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  }
+  __device__ static void swap32(uint32_t v, uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  }
+  __device__ static uint32_t read(uint32_t v, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+  }
+};
+// 64-bit values move as two 32-bit halves
+template <typename T64>
+struct LaneBits64 {
+  __device__ static uint64_t bits(T64 v) { return __builtin_bit_cast(uint64_t, v); }
+  __device__ static T64 val(uint32_t lo, uint32_t hi) {
+    return __builtin_bit_cast(T64, ((uint64_t)hi << 32) | lo);
+  }
+  template <int CTRL, int RM = 0xF>
+  __device__ static T64 dpp(T64 v) {
+    const uint64_t b = bits(v);
+    return val(dpp_u32<CTRL, RM>((uint32_t)b), dpp_u32<CTRL, RM>((uint32_t)(b >> 32)));
+  }
+  __device__ static void swap16(T64 v, T64& a, T64& b) {
+    const uint64_t x = bits(v);
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+    a = val(lo[0], hi[0]);
+    b = val(lo[1], hi[1]);
+  }
+  __device__ static void swap32(T64 v, T64& a, T64& b) {
+    const uint64_t x = bits(v);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+    a = val(lo[0], hi[0]);
+    b = val(lo[1], hi[1]);
+  }
+  __device__ static T64 read(T64 v, int l) {
+    const uint64_t b = bits(v);
+    return val((uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l),
+               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l));
+  }
+};
+template <>
+struct LaneBits<double> : LaneBits64<double> {};
+template <>
+struct LaneBits<int64_t> : LaneBits64<int64_t> {};
+template <>
+struct LaneBits<unsigned long long> : LaneBits64<unsigned long long> {};
+
+// Butterfly over groups of `width` consecutive lanes (a power of two <= 64,
+// wave-uniform): every lane of a group gets op over the group.
+template <typename T, typename Op>
+__device__ __forceinline__ T group_reduce(T v, int width, Op op) {
+  using LB = LaneBits<T>;
+  if (width > 1) v = op(v, LB::template dpp<kDppQuadXor1>(v));
+  if (width > 2) v = op(v, LB::template dpp<kDppQuadXor2>(v));
+  if (width > 4) v = op(v, LB::template dpp<kDppHalfMirror>(v));
+  if (width > 8) v = op(v, LB::template dpp<kDppMirror>(v));
+  if (width > 16) {
+    T a, b;
+    LB::swap16(v, a, b);
+    v = op(a, b);
+  }
+  if (width > 32) {
+    T a, b;
+    LB::swap32(v, a, b);
+    v = op(a, b);
+  }
+  return v;
+}
+
+struct OpAdd {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct OpOr {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; }
+};
+struct OpMax {   // maximum that ignores NaN operands
+  __device__ float operator()(float a, float b) const { return fmax_nan_ignoring(a, b); }
+};
+struct OpMaxI64 {
+  __device__ int64_t operator()(int64_t a, int64_t b) const { return a > b ? a : b; }
+};
+
 template <typename T>
 __device__ __forceinline__ T wave_xor_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return group_reduce(v, 64, OpAdd());
 }
 
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o);
-  return v;
+  return group_reduce(v, 64, OpOr());
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmax_nan_ignoring(v, __shfl_xor(v, o));
+  return group_reduce(v, 64, OpMax());
+}
+
+// Value of lane l (wave-uniform l) in every lane.
+template <typename T>
+__device__ __forceinline__ T lane_value(T v, int l) {
+  return LaneBits<T>::read(v, l);
+}
+
+// Inclusive scan over the 64 lanes, fixed order: Hillis-Steele within each
+// row of 16 lanes, then each row's total is carried into the rows after it
+// (row 0 into row 1 and row 2 into row 3, then rows 0-1 into rows 2-3).
+template <typename T>
+__device__ __forceinline__ T wave_scan(T v) {
+  using LB = LaneBits<T>;
+  v += LB::template dpp<kDppRowShr + 1>(v);
+  v += LB::template dpp<kDppRowShr + 2>(v);
+  v += LB::template dpp<kDppRowShr + 4>(v);
+  v += LB::template dpp<kDppRowShr + 8>(v);
+  v += LB::template dpp<kDppBcast15, 0xA>(v);
+  v += LB::template dpp<kDppBcast31, 0xC>(v);
   return v;
 }
 
-// Inclusive Hillis-Steele scan over the 64 lanes, fixed order.
 __device__ __forceinline__ double wave_incl_scan(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    double t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
+  (void)lane;
+  return wave_scan(v);
 }
 
 __device__ __forceinline__ void status_or(uint32_t* status, uint32_t bits) {
@@ -237,6 +383,25 @@ __device__ __forceinline__ void load_task(const void* rp, int64_t chunk, int64_t
   }
 }
 
+// One residual tile (2048 logits) of a row for one wave: lane l gets groups
+// l, l+64, l+128, l+192 of the tile (each 16-byte load instruction covers
+// 1 KB of contiguous logits); past V: all -inf.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_tile(const void* row, int64_t t, int64_t V, int lane,
+                                          GroupRaw<DT> raw[kTileGroupsPerLane]) {
+  const int64_t g0 = t * kTileGroups;
+  if (VEC && (t + 1) * kTileElems <= V) {
+    // the whole tile is inside the row: no per-group bounds checks
+#pragma unroll
+    for (int j = 0; j < kTileGroupsPerLane; ++j)
+      load_full_nt<DT>(row, (g0 + j * 64 + lane) * kGroup, raw[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTileGroupsPerLane; ++j)
+      load_group<DT, VEC>(row, g0 + j * 64 + lane, V, raw[j]);
+  }
+}
+
 // Exact maximum m and s = sum 2^(y_k) of one wave task (all lanes get both).
 template <int DT, bool CHECK>
 __device__ __forceinline__ void task_stats(const GroupRaw<DT> raw[kTaskGroupsPerLane],
@@ -333,14 +498,13 @@ __device__ __forceinline__ Partial load_partial(const Partial* __restrict__ part
 
 // Row maximum and normaliser from one partial per lane, L lanes per row.
 __device__ __forceinline__ RowNorm reduce_partials(const Partial& p, int L, const ExpConsts& ec) {
-  float M = p.m;
-  for (int o = L >> 1; o > 0; o >>= 1) M = fmax_nan_ignoring(M, __shfl_xor(M, o));
+  const float M = group_reduce(p.m, L, OpMax());
   double s = 0.0;
   if (p.m != -INFINITY) {
     const double K = offset_of(p.m, shift_of(p.m, ec), ec);
     s = p.s * exp2(((double)p.m - (double)M) * ec.c64 - K);
   }
-  for (int o = L >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  s = group_reduce(s, L, OpAdd());
   RowNorm r;
   r.M = M;
   r.s = s;
@@ -364,8 +528,7 @@ __device__ __forceinline__ RowNorm combine_rows_packed(const Partial* __restrict
     p.m = -INFINITY;
     p.s = 0.0;
     if (have) p = part[row * tpr + sub];
-    M = p.m;
-    for (int o = L >> 1; o > 0; o >>= 1) M = fmax_nan_ignoring(M, __shfl_xor(M, o));
+    M = group_reduce(p.m, L, OpMax());
     if (have && p.m != -INFINITY) {
       const double K = offset_of(p.m, shift_of(p.m, ec), ec);
       s = p.s * exp2(((double)p.m - (double)M) * ec.c64 - K);
@@ -373,7 +536,7 @@ __device__ __forceinline__ RowNorm combine_rows_packed(const Partial* __restrict
   } else {
     if (active)
       for (int64_t i = sub; i < tpr; i += L) M = fmax_nan_ignoring(M, part[row * tpr + i].m);
-    for (int o = L >> 1; o > 0; o >>= 1) M = fmax_nan_ignoring(M, __shfl_xor(M, o));
+    M = group_reduce(M, L, OpMax());
     if (active) {
       for (int64_t i = sub; i < tpr; i += L) {
         const Partial p = part[row * tpr + i];
@@ -383,7 +546,7 @@ __device__ __forceinline__ RowNorm combine_rows_packed(const Partial* __restrict
       }
     }
   }
-  for (int o = L >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  s = group_reduce(s, L, OpAdd());
   RowNorm r;
   r.M = M;
   r.s = s;
@@ -470,7 +633,7 @@ __device__ __forceinline__ double wave_total(const double* v, int64_t n, int lan
   double total = 0.0;
   for (int64_t c = 0; c < n; c += 64) {
     const double x = (c + lane < n) ? v[c + lane] : 0.0;
-    total += __shfl(wave_incl_scan(x, lane), 63);
+    total += lane_value(wave_incl_scan(x, lane), 63);
   }
   return total;
 }
@@ -490,9 +653,9 @@ __device__ __forceinline__ void find_interval(const double* v, int64_t n, double
     if (hit) {
       const int l = __builtin_ctzll(hit);
       tau = c + l;
-      p_excl = __shfl(lane == 0 ? base : below, l);
+      p_excl = lane_value(lane == 0 ? base : below, l);
     }
-    base = __shfl(incl, 63);
+    base = lane_value(incl, 63);
   }
   if (tau < 0) {
     // t at or past the rounded total: the last interval with mass
@@ -550,13 +713,9 @@ __device__ __forceinline__ int64_t block_search_weights(const float w[kGroup], i
   int64_t cand = -1;
   if (hit) {
     const int l = __builtin_ctzll(hit);
-    cand = (gi - lane + l) * kGroup + __shfl(k_hit, l);
+    cand = (gi - lane + l) * kGroup + (int)lane_value((uint32_t)k_hit, l);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int64_t ol = __shfl_xor(last_pos, o);
-    last_pos = ol > last_pos ? ol : last_pos;
-  }
+  last_pos = group_reduce(last_pos, 64, OpMaxI64());
   if (lane == 0) {
     ds.cand[wave] = cand;
     ds.last_pos[wave] = last_pos;
@@ -589,7 +748,7 @@ __device__ __forceinline__ int64_t block_search(const GroupRaw<DT>& rp, const Gr
 __device__ __forceinline__ double block_sum(double v, DrawShared& ds) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const double ws = __shfl(wave_incl_scan(v, lane), 63);
+  const double ws = lane_value(wave_incl_scan(v, lane), 63);
   if (lane == 0) ds.red[wave] = ws;
   __syncthreads();
   double t = 0.0;
@@ -948,12 +1107,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     double* ts_seq = tile_sums + b * num_tiles;
     for (int64_t t = t_lo + wave; t < t_hi; t += kWaves) {
       GroupRaw<DT> cp[kTileGroupsPerLane], cq[kTileGroupsPerLane];
-#pragma unroll
-      for (int j = 0; j < kTileGroupsPerLane; ++j) {
-        const int64_t gi = t * kTileGroups + j * 64 + lane;   // past V: all -inf
-        load_group<DT, VEC>(prow, gi, V, cp[j]);
-        load_group<DT, VEC>(qrow, gi, V, cq[j]);
-      }
+      load_tile<DT, VEC>(prow, t, V, lane, cp);
+      load_tile<DT, VEC>(qrow, t, V, lane, cq);
       float lsum = 0.0f;
 #pragma unroll
       for (int j = 0; j < kTileGroupsPerLane; ++j) {

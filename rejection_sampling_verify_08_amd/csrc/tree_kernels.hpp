@@ -292,7 +292,7 @@ __device__ __forceinline__ void gather_slots(TreePointShared& sh, double* slot_t
     bool first_x = act, first_t = act;
     int first_lane = lane;
     for (int j = cnt - 1; j >= 0; --j) {
-      const int32_t xj = __shfl(x, j);
+      const int32_t xj = (int32_t)lane_value((uint32_t)x, j);
       if (j < lane && xj == x) {
         first_x = false;
         first_lane = j;
@@ -401,7 +401,7 @@ __device__ __forceinline__ void gather_slots(TreePointShared& sh, double* slot_t
       double v = c < tpr ? ts[c] : 0.0;
       for (int j = 0; j < nt; ++j)
         if (sh.xtask[k0 + j] == c) v = sh.xsum[k0 + j];
-      total += __shfl(wave_incl_scan(v, lane), 63);
+      total += lane_value(wave_incl_scan(v, lane), 63);
     }
     if (lane == 0) sh.slot_rest[wave] = total;
   }
@@ -541,18 +541,14 @@ __global__ __launch_bounds__(kThreads) void tree_point_kernel(
         break;
       }
       // flat ranges in node order
-      int before = nk;
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(before, o);
-        if (lane >= o) before += t;
-      }
+      const int before = (int)wave_scan((uint32_t)nk);
       if (nk > 0) {
         const int sl = ns + __builtin_popcountll(m & ((1ull << lane) - 1));
         sh.slot_node[sl] = (int32_t)n;
         sh.slot_k0[sl] = k0 + before - nk;
       }
       ns += __builtin_popcountll(m);
-      k0 += __shfl(before, 63);
+      k0 += (int)lane_value((uint32_t)before, 63);
     }
     if (lane == 0) {
       sh.prefetch = fits ? 1 : 0;
