@@ -118,8 +118,9 @@ def cpu_baseline(inp, budget_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    # the GPU reaches its steady clocks only after ~0.1-0.2 s of this load
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--config", type=int, default=3, help="named workload 1..5")
     ap.add_argument("--sets", type=int, default=3, help="rotating device input copies")
     ap.add_argument("--cpu-budget", type=float, default=12.0,

@@ -32,6 +32,7 @@ struct ArgPartial {     // one wave task of one target row
   float v;              // the task's maximum (-inf when every logit is -inf)
   int32_t k;            // lowest logit index holding it
 };
+static_assert(sizeof(ArgPartial) == 8, "stored as one 8-byte vector");
 
 // (v, k) beats (bv, bk): larger value, or equal value and lower index.
 // NaN never beats anything.
@@ -117,10 +118,10 @@ __global__ __launch_bounds__(kStatsThreads) void argmax_kernel(
   wave_argmax(bv, bk);
   if (CHECK) bad = wave_or(bad);
   if (lane == 0) {
-    ArgPartial p;
-    p.v = bv;
-    p.k = (int32_t)bk;
-    partials[task] = p;
+    // non-temporal, as the row-statistics partials
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 pv = {__float_as_uint(bv), (uint32_t)(int32_t)bk};
+    __builtin_nontemporal_store(pv, reinterpret_cast<u32x2*>(partials + task));
     if (CHECK) status_or(status, bad);
   }
 }
