@@ -616,6 +616,7 @@ struct SeqShared {
   int n;                 // accepted count
   int skip;              // nonzero: a bad draft token, the sequence is skipped
   uint32_t bad;
+  int tile_next;         // residual tiles handed out past each wave's first
 };
 
 // ---------------------------------------------------------------- the draw
@@ -903,6 +904,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     sh.bad = 0;
     sh.n = (int)gamma;
     sh.skip = 0;
+    sh.tile_next = 0;
   }
   __syncthreads();
 
@@ -1104,11 +1106,15 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     // ---- tile sums of this workgroup's share of the tiles.  A tile is 2048
     // logits: 256 consecutive groups, lane l holding groups l, l+64, l+128,
     // l+192 (each 16-byte load instruction covers 1 KB of contiguous logits).
+    // Wave w takes tile t_lo + w first, then the next unclaimed tile from an
+    // LDS counter: waves progress at different rates (two share a SIMD), and
+    // a static round-robin left the last wave of a workgroup ~4.6 us behind
+    // its first.  A tile's sum does not depend on the wave that computes it.
     const int64_t per = (num_tiles + G - 1) / G;
     const int64_t t_lo = (int64_t)g * per;
     const int64_t t_hi = t_lo + per < num_tiles ? t_lo + per : num_tiles;
     double* ts_seq = tile_sums + b * num_tiles;
-    for (int64_t t = t_lo + wave; t < t_hi; t += kWaves) {
+    for (int64_t t = t_lo + wave; t < t_hi;) {
       GroupRaw<DT> cp[kTileGroupsPerLane], cq[kTileGroupsPerLane];
       load_tile<DT, VEC>(prow, t, V, lane, cp);
       load_tile<DT, VEC>(qrow, t, V, lane, cq);
@@ -1120,10 +1126,13 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
         lsum += seq_sum8(w);
       }
       const double ts = wave_xor_sum((double)lsum);
+      int claimed = 0;
       if (lane == 0) {
         if (G == 1) tile_sum[t] = ts;
         else __hip_atomic_store(&ts_seq[t], ts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        claimed = atomicAdd(&sh.tile_next, 1);
       }
+      t = t_lo + kWaves + (int64_t)__builtin_amdgcn_readfirstlane(claimed);
     }
     // ---- arrival: with G > 1 the tile sums cross workgroups.  They were
     // written with agent-scope atomic stores (through to the device-coherent
