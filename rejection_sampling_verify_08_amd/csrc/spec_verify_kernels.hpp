@@ -404,7 +404,36 @@ __device__ __forceinline__ void load_tile(const void* row, int64_t t, int64_t V,
   }
 }
 
+// 2^y in double for y below ~1000, y = -inf, NaN or below -1100 giving 0:
+// y = n + f with n = rint(y) and |f| <= 1/2; 2^f from the degree-8
+// polynomial that interpolates it at the Chebyshev nodes of [-1/2, 1/2]
+// (coefficients computed in 40-digit arithmetic; relative error of the
+// polynomial below 1.1e-12 on the interval), scaled by 2^n.  The
+// coefficients sit in constant memory so that they load once into scalar
+// registers; there is no branch.
+__constant__ double kExp2Poly[9] = {   // highest degree first
+    1.3255224878668817e-06, 1.5310079402249296e-05, 0.00015403455852453838,
+    0.0013333450568000645,  0.009618129159402558,   0.05550410941205933,
+    0.2402265069581299,     0.6931471805459335,     1.0};
+__device__ __forceinline__ double exp2_accurate(double y) {
+  // fmax drops a NaN; 2^-1100 underflows to 0
+  const double yc = __builtin_fmax(y, -1100.0);
+  const double n = __builtin_rint(yc);
+  const double f = yc - n;
+  double e = kExp2Poly[0];
+#pragma unroll
+  for (int i = 1; i < 9; ++i) e = __builtin_fma(e, f, kExp2Poly[i]);
+  return __builtin_ldexp(e, (int)n);
+}
+
 // Exact maximum m and s = sum 2^(y_k) of one wave task (all lanes get both).
+// fp32 logits take every term in double: y_k = l_k c_hi + A + l_k c_lo
+// without rounding and 2^(y_k) to ~1e-12.  The ratio of two rows'
+// normalisers enters the residual draw, and when the draft row is within a
+// few thousandths of the target row the residual is a small difference of
+// two near-equal distributions: float terms (one rounding of y_k, ~3e-8 per
+// exponential) left its sum up to ~2.4e-5 off.  bf16 logits keep the float
+// terms (their residual tolerance is 2e-3).
 template <int DT, bool CHECK>
 __device__ __forceinline__ void task_stats(const GroupRaw<DT> raw[kTaskGroupsPerLane],
                                            const ExpConsts& ec, float& m_out, double& s_out,
@@ -423,15 +452,31 @@ __device__ __forceinline__ void task_stats(const GroupRaw<DT> raw[kTaskGroupsPer
   m = wave_max(m);
   const float A = shift_of(m, ec);
   double acc = 0.0;
+  if constexpr (DT == 0) {
+    const double chd = ec.c_hi, cld = ec.c_lo, Ad = A;
 #pragma unroll
-  for (int j = 0; j < kTaskGroupsPerLane; ++j) {
-    float v[kGroup];
-    unpack<DT>(raw[j], v);
-    float e[kGroup];
+    for (int j = 0; j < kTaskGroupsPerLane; ++j) {
+      float v[kGroup];
+      unpack<DT>(raw[j], v);
+      double e[kGroup];
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) e[k] = exp_term(v[k], A, ec);
-    const float s8 = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    acc += (double)s8;
+      for (int k = 0; k < kGroup; ++k) {
+        const double l = v[k];
+        e[k] = exp2_accurate(__builtin_fma(l, cld, __builtin_fma(l, chd, Ad)));
+      }
+      acc += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTaskGroupsPerLane; ++j) {
+      float v[kGroup];
+      unpack<DT>(raw[j], v);
+      float e[kGroup];
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) e[k] = exp_term(v[k], A, ec);
+      const float s8 = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      acc += (double)s8;
+    }
   }
   m_out = m;
   s_out = wave_xor_sum(acc);
@@ -567,9 +612,25 @@ constexpr int kDrawPoint = 2;      // draft distribution is the point mass at x
 struct DrawConsts {
   float Ap, Aq;          // per-row shifts
   float rho_hi, rho_lo;  // rho = (s_p / s_q) 2^(Kp - Kq), split
+  float C_hi, C_lo;      // C = (Mq - Mp) c - log2(s_p / s_q), split (fp32 residuals)
   int residual;          // kDrawBonus, kDrawResidual or kDrawPoint
   int64_t x;             // kDrawPoint: the rejected draft token
 };
+
+// 1 - 2^-d for d > 0 with a small relative error: below 1/2 the Taylor
+// series of 1 - e^-u in u = d ln 2 (the direct form would cancel), evaluated
+// innermost first and truncated after the u^8 term (relative remainder
+// < 6e-10); exp2 above.
+__device__ __forceinline__ float one_minus_exp2_neg(float d) {
+  if (d < 0.5f) {
+    const float u = d * 0.693147182f;   // ln 2 in float
+    float t = 1.0f;
+#pragma unroll
+    for (int n = 8; n >= 2; --n) t = __builtin_fmaf(-u * (1.0f / (float)n), t, 1.0f);
+    return u * t;
+  }
+  return 1.0f - __builtin_amdgcn_exp2f(-d);
+}
 
 // rp/rq hold group g of the p and q rows (rq unused unless kDrawResidual);
 // e0 = 8 g is the group's first logit index.
@@ -588,13 +649,29 @@ __device__ __forceinline__ void weights_of(const GroupRaw<DT>& rp, const GroupRa
   } else if (dc.residual == kDrawResidual) {
     float lq[kGroup];
     unpack<DT>(rq, lq);
+    if constexpr (DT == 0) {
+      // fp32 logits: p - q = p (1 - 2^-d) with d = log2(p/q) =
+      // (l_p - l_q) c + C.  l_p - l_q is exact when the two are close, so a
+      // residual made of small differences keeps its relative precision
+      // (e_p - rho e_q would lose it to cancellation).
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
-      const float ep = exp_term(lp[k], dc.Ap, ec);
-      const float eq = exp_term(lq[k], dc.Aq, ec);
-      float d = __builtin_fmaf(-eq, dc.rho_hi, ep);
-      d = __builtin_fmaf(-eq, dc.rho_lo, d);
-      w[k] = d > 0.0f ? d : 0.0f;
+      for (int k = 0; k < kGroup; ++k) {
+        const float ep = exp_term(lp[k], dc.Ap, ec);
+        const float dl = lp[k] - lq[k];
+        float d = __builtin_fmaf(dl, ec.c_hi, dc.C_hi);
+        d = __builtin_fmaf(dl, ec.c_lo, d);
+        d = d + dc.C_lo;
+        w[k] = (ep > 0.0f && d > 0.0f) ? ep * one_minus_exp2_neg(d) : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        const float ep = exp_term(lp[k], dc.Ap, ec);
+        const float eq = exp_term(lq[k], dc.Aq, ec);
+        float d = __builtin_fmaf(-eq, dc.rho_hi, ep);
+        d = __builtin_fmaf(-eq, dc.rho_lo, d);
+        w[k] = d > 0.0f ? d : 0.0f;
+      }
     }
   } else {
 #pragma unroll
@@ -1088,10 +1165,16 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     const double rho = (sp / sq) * exp2(Kp - offset_of(Mq, dc.Aq, ec));
     dc.rho_hi = (float)rho;
     dc.rho_lo = (float)(rho - (double)dc.rho_hi);
+    const double C = ((double)Mq - (double)Mp) * ((double)ec.c_hi + (double)ec.c_lo) -
+                     log2(sp / sq);
+    dc.C_hi = (float)C;
+    dc.C_lo = (float)(C - (double)dc.C_hi);
   } else {
     dc.Aq = 0.0f;
     dc.rho_hi = 0.0f;
     dc.rho_lo = 0.0f;
+    dc.C_hi = 0.0f;
+    dc.C_lo = 0.0f;
   }
   __shared__ DrawShared ds;
   uint32_t fbad = sh.bad;

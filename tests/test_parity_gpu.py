@@ -113,6 +113,27 @@ def test_ragged_batch_with_long_drafts():
     _check(inp2, "gamma up to 70, draft == target")
 
 
+@pytest.mark.parametrize("V,dtype,noise,B", [(71, W.F32, 0.0054, 400), (4925, W.F32, 0.0086, 200),
+                                             (4925, W.BF16, 0.0086, 150)])
+def test_near_identical_draft_rows(V, dtype, noise, B):
+    """Draft rows within a few thousandths of the target rows (alpha > 0.99):
+    a rejection's residual max(0, p - q) is then a small difference of two
+    near-equal distributions, ~1e-3 of the mass, and its sum must still meet
+    the relative tolerance (1e-5 for fp32 inputs).  Heavy rows (a few
+    boosted tokens dominate), long drafts so that rejections occur."""
+    rng = np.random.default_rng(V)
+    gam = rng.integers(20, 41, size=B)
+    inp = W.build(f"near-identical V={V}", 70_000 + V, gam, V, dtype, 1.4,
+                  W.boosted_random_ids_rows(3.0, min(20, V), 8.0), noise)
+    label = f"near-identical draft rows V={V} {dtype} noise={noise}"
+    log(f"[case] {label}: B={inp.num_seqs} R_t={inp.target_rows}")
+    ora = oracle.verify_inputs(inp)
+    assert (np.asarray(ora.num_accepted) < gam).sum() >= 5   # residual draws occur
+    gpu = run_gpu(inp)
+    compare(inp, gpu, ora, label=label)
+    assert gpu.status == 0
+
+
 def test_identical_rows_always_accepted():
     inp = W.build("ident", 3, [4] * 64, 128256, W.BF16, 1.0,
                   W.boosted_top_rows(2.0, 50, 6.0), 0.0, draft_copy=lambda b: True)
