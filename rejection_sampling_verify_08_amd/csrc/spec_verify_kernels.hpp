@@ -1165,10 +1165,15 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     const double rho = (sp / sq) * exp2(Kp - offset_of(Mq, dc.Aq, ec));
     dc.rho_hi = (float)rho;
     dc.rho_lo = (float)(rho - (double)dc.rho_hi);
-    const double C = ((double)Mq - (double)Mp) * ((double)ec.c_hi + (double)ec.c_lo) -
-                     log2(sp / sq);
-    dc.C_hi = (float)C;
-    dc.C_lo = (float)(C - (double)dc.C_hi);
+    if constexpr (DT == 0) {   // only the fp32 weights use C
+      const double C = ((double)Mq - (double)Mp) * ((double)ec.c_hi + (double)ec.c_lo) -
+                       log2(sp / sq);
+      dc.C_hi = (float)C;
+      dc.C_lo = (float)(C - (double)dc.C_hi);
+    } else {
+      dc.C_hi = 0.0f;
+      dc.C_lo = 0.0f;
+    }
   } else {
     dc.Aq = 0.0f;
     dc.rho_hi = 0.0f;
