@@ -24,8 +24,9 @@
 //     y_k = (l_k - m) log2(e)/T + K up to one rounding of |y_k|, where
 //     K = (A + m c_hi) + m c_lo is a per-task constant known exactly in
 //     double that later steps divide out.  Sums of 8 terms are fp32,
-//     everything above is fp64 in a fixed order.  Each wave task writes one
-//     partial {m, s}.
+//     everything above is fp64 in a fixed order (fp32 logits: every term in
+//     double, y_k unrounded).  Each wave task writes one partial {m, s} with
+//     a non-temporal store.
 //
 //   finish_kernel (G 512-thread workgroups per sequence): each combines
 //     the partials into exact row maxima M and normalisers s in double,
@@ -33,7 +34,8 @@
 //     lowest lane of a wave ballot of !(u_i < r_i) ([A] 1.2 step 3, [D] 2.1:
 //     the first rejection ends the test).  A residual w_k = max(0, p_k - q_k)
 //     needs both rows again: the G workgroups share one more read of the
-//     rejected target/draft pair, one double per 2048-logit tile, and the
+//     rejected target/draft pair, one double per 2048-logit tile (the tiles
+//     of a workgroup handed to its waves through an LDS counter), and the
 //     last workgroup to arrive (an integer counter cleared by the row pass)
 //     scans the tile sums for the tile holding t = u * S.  A bonus draw
 //     (w_k = p_k) and a point-mass residual (p with x removed) need no
