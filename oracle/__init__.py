@@ -97,7 +97,9 @@ class OracleResult:
     residual_sum: np.ndarray      # float64 [B]
     tie_accept: np.ndarray        # float64 [R_d], NaN where not evaluated
     tie_final: np.ndarray         # float64 [B]
-    flagged: np.ndarray           # int32 [B], nonzero = within the tie window
+    flagged: np.ndarray           # int32 [B], nonzero = within the tie window (bit0 accept
+                                  # test, bit1 final draw, bit2 empty residual, bit3 residual
+                                  # mass below 2^-20)
 
     def emitted(self, b: int, cu: np.ndarray) -> np.ndarray:
         t0 = int(cu[b]) + b

@@ -51,7 +51,11 @@
  *
  * Diagnostics: the distance |u_i - r_i| of every evaluated test, and for the
  * final draw min(t - C_{k-1}, C_k - t) / S; a sequence is flagged when any of
- * them is below `tie_tol` (the caller passes 1e-6).
+ * them is below `tie_tol` (the caller passes 1e-6).  A residual draw whose
+ * mass S is below 2^-20 is flagged as well: every threshold C_k / S then
+ * rests on differences p_k - q_k below 16 fp32 ulps of the unit mass, which
+ * a computation at fp32 precision does not resolve (the decision is not
+ * determined at the precision the logits are given in).
  *
  * Layout: packed ragged rows, cu[b] = sum of gamma_{b'} for b' < b; target
  * row of (b, i) is cu[b] + b + i, draft row is cu[b] + i; one uniform per
@@ -141,7 +145,8 @@ double oracle_overlap_mass(const void *target_row, const void *draft_row,
  *   tie_final[B]             double final-draw boundary distance (may be NULL)
  *   flagged[B]               int32 bit0: an accept test within tie_tol,
  *                            bit1: the final draw within tie_tol,
- *                            bit2: empty residual fallback (may be NULL)
+ *                            bit2: empty residual fallback,
+ *                            bit3: residual mass below 2^-20 (may be NULL)
  * Returns 0, or a negative code for invalid arguments / allocation failure.
  */
 int oracle_verify(int32_t num_seqs, const int32_t *cu_draft,
@@ -234,6 +239,7 @@ int oracle_verify(int32_t num_seqs, const int32_t *cu_draft,
     double S = 0.0;
     for (int64_t k = 0; k < vocab; ++k) { S += w[k]; C[k] = S; }
     const double S_reported = (j < gamma) ? S : 0.0;
+    if (j < gamma && S < 0x1p-20) flag |= 8;   /* residual below fp32 resolution */
     if (!(S > 0.0)) { /* empty residual: draw from p_j instead */
       flag |= 4;
       S = 0.0;

@@ -134,6 +134,56 @@ def test_near_identical_draft_rows(V, dtype, noise, B):
     assert gpu.status == 0
 
 
+def _masked_low_temperature_case(seed):
+    """Seeded masked batch at low temperature: -inf over a random share of
+    every row (at least one finite logit kept), a drafted token that the
+    mask hit restored at logit 1.0 (so its q is tiny), T near 0.05."""
+    rng = np.random.default_rng(150_000 + seed)
+    V = int(rng.choice([int(rng.integers(2, 300)), int(rng.integers(300, 9000)),
+                        int(rng.integers(9000, 70000))]))
+    B = int(rng.integers(1, 60))
+    gam = rng.integers(0, int(rng.choice([8, 20, 63])) + 1, size=B)
+    dtype = W.BF16 if rng.random() < 0.6 else W.F32
+    T = float(rng.choice([0.05, 0.2, 1.0, 3.0, 20.0])) * float(rng.uniform(0.8, 1.25))
+    gens = [W.iid_normal_rows(float(rng.uniform(0.3, 3.0))),
+            W.boosted_top_rows(2.0, max(1, min(50, V // 3)), 6.0),
+            W.boosted_random_ids_rows(3.0, max(1, min(20, V)), 8.0)]
+    gen = gens[int(rng.integers(0, 3))]
+    noise = float(rng.uniform(0.0, 2.0))
+    frac = float(rng.choice([0.0, 0.3, 0.9, 0.99]))
+    inp = W.build(f"masked {seed}", 160_000 + seed, gam, V, dtype, T, gen, noise)
+    neg = np.uint16(0xFF80) if dtype == W.BF16 else np.float32(-np.inf)
+    one = np.uint16(0x3F80) if dtype == W.BF16 else np.float32(1.0)
+    for arr in (inp.target_logits, inp.draft_logits):
+        if arr.shape[0] == 0 or frac == 0.0:
+            continue
+        arr[rng.random(arr.shape) < frac] = neg
+        for r in range(arr.shape[0]):
+            if (arr[r] == neg).all():
+                arr[r, int(rng.integers(0, V))] = one
+    for r, x in enumerate(inp.draft_tokens):
+        if inp.draft_logits[r, x] == neg:
+            inp.draft_logits[r, x] = one
+    return inp
+
+
+@pytest.mark.parametrize("seed", [149, 694, 1151])
+def test_residual_below_fp32_resolution(seed):
+    """Rejections whose residual mass is below 2^-20 (p and q near-identical
+    one-hot distributions at T ~ 0.05): the oracle flags them (bit 3), the
+    draw there is only required to be a valid token, the residual sum is not
+    compared, and the kernel may report an empty residual (status bit 6)."""
+    inp = _masked_low_temperature_case(seed)
+    label = f"residual below fp32 resolution, seed {seed}"
+    log(f"[case] {label}: B={inp.num_seqs} V={inp.vocab} {inp.dtype} T={inp.temperature:.4f}")
+    ora = oracle.verify_inputs(inp)
+    flags = np.asarray(ora.flagged)
+    assert (flags & 8).any()
+    gpu = run_gpu(inp)
+    compare(inp, gpu, ora, label=label)
+    assert gpu.status == 0 or (gpu.status == 64 and (flags & 12).any()), hex(gpu.status)
+
+
 def test_identical_rows_always_accepted():
     inp = W.build("ident", 3, [4] * 64, 128256, W.BF16, 1.0,
                   W.boosted_top_rows(2.0, 50, 6.0), 0.0, draft_copy=lambda b: True)
