@@ -56,7 +56,7 @@ struct spec_verify_ctx {
   uint32_t flags;
   int cu_count;
   int64_t tasks_per_row;   // wave tasks of 4096 logits per row
-  int64_t num_tiles;       // 512-logit tiles per row (tile sums live in LDS)
+  int64_t num_tiles;       // 2048-logit residual tiles per row
   Layout layout;
 };
 
@@ -145,10 +145,12 @@ hipError_t launch_sampled(const spec_verify_ctx* ctx, const spec_verify_args* a,
   if (e != hipSuccess) return e;
 
   // kernel 2: G workgroups per sequence, about one per compute unit in all,
-  // sharing a residual's second pass over its rows.  Point-mass drafts never
-  // make that pass (their draws use the row pass's task sums): one each.
+  // sharing a residual's second pass over its rows, with at least two tiles
+  // each (at B = 1-4 and V = 128256, 32 workgroups of two tiles finish
+  // ~1 us sooner than 63 of one).  Point-mass drafts never make that pass
+  // (their draws use the row pass's task sums): one each.
   int64_t G = ctx->cu_count / B;
-  if (G > ctx->num_tiles) G = ctx->num_tiles;
+  if (G > (ctx->num_tiles + 1) / 2) G = (ctx->num_tiles + 1) / 2;
   if (G < 1 || MODE == kDraftPoint) G = 1;
   const size_t lds = (size_t)ctx->num_tiles * sizeof(double);
   return launch(finish_kernel<DT, VEC, CHECK, MODE>, dim3((unsigned)(B * G)), dim3(kThreads), lds,
