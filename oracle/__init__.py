@@ -49,7 +49,7 @@ def _load():
         lib.oracle_verify.argtypes = [
             ctypes.c_int32, P, P, P, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int, P, P, ctypes.c_float, ctypes.c_double,
-            P, P, P, P, P, P, P, P]
+            P, P, P, P, P, P, P, P, P]
         lib.oracle_row_softmax.restype = ctypes.c_int
         lib.oracle_row_softmax.argtypes = [P, ctypes.c_int, ctypes.c_int64,
                                            ctypes.c_float, P]
@@ -59,7 +59,7 @@ def _load():
         lib.oracle_verify_onehot.restype = ctypes.c_int
         lib.oracle_verify_onehot.argtypes = [
             ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, P, P,
-            ctypes.c_float, ctypes.c_double, P, P, P, P, P, P, P]
+            ctypes.c_float, ctypes.c_double, P, P, P, P, P, P, P, P]
         lib.oracle_verify_tree_greedy.restype = ctypes.c_int
         lib.oracle_verify_tree_greedy.argtypes = [ctypes.c_int32, P, P, P, P, ctypes.c_int64,
                                                   ctypes.c_int64, ctypes.c_int, P, P, P]
@@ -95,11 +95,13 @@ class OracleResult:
     p_draft: np.ndarray           # float64 [R_d]
     q_draft: np.ndarray           # float64 [R_d]
     residual_sum: np.ndarray      # float64 [B]
-    tie_accept: np.ndarray        # float64 [R_d], NaN where not evaluated
-    tie_final: np.ndarray         # float64 [B]
-    flagged: np.ndarray           # int32 [B], nonzero = within the tie window (bit0 accept
-                                  # test, bit1 final draw, bit2 empty residual, bit3 residual
-                                  # mass below 2^-20)
+    tie_accept: np.ndarray        # float64 [R_d], |u - r| less r's error bound (>= 0),
+                                  # NaN where not evaluated
+    tie_final: np.ndarray         # float64 [B], final-draw boundary distance less E (>= 0)
+    final_err: np.ndarray         # float64 [B], E: bound on the error of every C_k / S
+    flagged: np.ndarray           # int32 [B], nonzero = a decision within the tie window
+                                  # widened by its error bound (bit0 accept test, bit1
+                                  # final draw, bit2 empty residual, bit3 E > tie / 10)
 
     def emitted(self, b: int, cu: np.ndarray) -> np.ndarray:
         t0 = int(cu[b]) + b
@@ -137,6 +139,7 @@ def verify(num_seqs: int, cu_draft, target_logits, draft_logits, draft_tokens,
         residual_sum=np.zeros(B, dtype=np.float64),
         tie_accept=np.full(R_d, np.nan, dtype=np.float64),
         tie_final=np.zeros(B, dtype=np.float64),
+        final_err=np.zeros(B, dtype=np.float64),
         flagged=np.zeros(B, dtype=np.int32))
     rc = lib.oracle_verify(
         B, _ptr(cu), _ptr(tgt), _ptr(dft), ld, V, code, _ptr(tok), _ptr(u),
@@ -144,7 +147,7 @@ def verify(num_seqs: int, cu_draft, target_logits, draft_logits, draft_tokens,
         _ptr(res.num_accepted), _ptr(res.p_draft) if R_d else None,
         _ptr(res.q_draft) if R_d else None, _ptr(res.residual_sum),
         _ptr(res.tie_accept) if R_d else None, _ptr(res.tie_final),
-        _ptr(res.flagged))
+        _ptr(res.final_err), _ptr(res.flagged))
     if rc != 0:
         raise ValueError(f"oracle_verify returned {rc}")
     return res
@@ -241,12 +244,14 @@ def verify_onehot(num_seqs: int, cu_draft, target_logits, draft_tokens, uniforms
         residual_sum=np.zeros(B, dtype=np.float64),
         tie_accept=np.full(R_d, np.nan, dtype=np.float64),
         tie_final=np.zeros(B, dtype=np.float64),
+        final_err=np.zeros(B, dtype=np.float64),
         flagged=np.zeros(B, dtype=np.int32))
     rc = lib.oracle_verify_onehot(
         B, _ptr(cu), _ptr(tgt), ld, V, code, _ptr(tok), _ptr(u), float(temperature),
         float(tie_tol), _ptr(res.out_tokens), _ptr(res.num_accepted),
         _ptr(res.p_draft) if R_d else None, _ptr(res.residual_sum),
-        _ptr(res.tie_accept) if R_d else None, _ptr(res.tie_final), _ptr(res.flagged))
+        _ptr(res.tie_accept) if R_d else None, _ptr(res.tie_final), _ptr(res.final_err),
+        _ptr(res.flagged))
     if rc != 0:
         raise ValueError(f"oracle_verify_onehot returned {rc}")
     return res

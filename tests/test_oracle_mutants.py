@@ -17,6 +17,7 @@ import oracle
 from tests import test_oracle_pins as pins
 from tests import test_oracle_pins_modes as mpins
 from tests import test_oracle_pins_tree as tpins
+from tests import test_oracle_pins_precision as ppins
 
 MUTANTS = [
     ("accept test in the wrong direction",
@@ -36,11 +37,14 @@ MUTANTS = [
     ("inverse CDF admits a zero-weight token",
      "if (C[k] > t) { tok = k; break; }", "if (C[k] >= t) { tok = k; break; }"),
     ("normaliser drops the first term",
-     "  double s = 0.0;\n  for (int64_t k = 0; k < vocab; ++k) {",
-     "  double s = 0.0;\n  for (int64_t k = 1; k < vocab; ++k) {"),
+     "  double err = 0.0;\n  for (int64_t k = 0; k < vocab; ++k) {",
+     "  double err = 0.0;\n  for (int64_t k = 1; k < vocab; ++k) {"),
     ("temperature multiplies instead of divides",
-     "return exp(load_logit(base, dtype, row * ld + k) / T - M) / s;",
-     "return exp(load_logit(base, dtype, row * ld + k) * T - M) / s;"),
+     "const double z = load_logit(base, dtype, row * ld + k) / T;",
+     "const double z = load_logit(base, dtype, row * ld + k) * T;"),
+    ("compensated sum drops its correction",
+     "static double csum_value(const csum *a) { return a->hi + a->lo; }",
+     "static double csum_value(const csum *a) { return a->hi; }"),
     ("target rows without the per-sequence offset",
      "const int64_t trow0 = (int64_t)cu_draft[b] + b;",
      "const int64_t trow0 = (int64_t)cu_draft[b];"),
@@ -86,9 +90,9 @@ TREE_MUTANTS = [
      "if (parent[g0 + n] == cur && tokens[g0 + n] == a)",
      "if (parent[g0 + n] == 0 && tokens[g0 + n] == a)"),
     ("tree point: no renormalisation after a rejection", TPOINT,
-     "r = p[x] / rest;", "r = p[x];"),
+     "r = p[x] / csum_value(&rest);", "r = p[x];"),
     ("tree point: rejected tokens kept in the final draw", TPOINT,
-     "S += removed[k] ? 0.0 : p[k];", "S += p[k];"),
+     "w[k] = removed[k] ? 0.0 : p[k];", "w[k] = p[k];"),
     ("tree point: a repeated token tested again", TPOINT,
      "r = 0.0;                     /* already rejected: p'(x) = 0 */",
      "r = p[x];"),
@@ -132,6 +136,7 @@ FAST_PINS = [
     (pins.test_exact_enumeration_output_law, {}),
     (pins.test_edge_cases, {}),
     (pins.test_tie_flags, {}),
+    (ppins.test_compensated_normaliser_keeps_sub_ulp_tail, {}),
 ]
 
 
