@@ -126,6 +126,12 @@ extern "C" {
                                             SPEC_VERIFY_MAX_TREE_CHILDREN children
                                             of one node; the sequence is skipped */
 
+#define SPEC_VERIFY_DEV_RESIDUAL_UNRESOLVED 256u /* a residual whose mass is below
+                                              2^-60 of the target row's: fp32
+                                              terms below 2^-126 may be a share
+                                              of it, so the draw is from its
+                                              representable part */
+
 /* Tree limits (per sequence). */
 #define SPEC_VERIFY_MAX_TREE_NODES 1024
 #define SPEC_VERIFY_MAX_TREE_CHILDREN 64

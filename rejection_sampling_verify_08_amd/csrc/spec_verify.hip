@@ -40,7 +40,7 @@ int hip_fail(hipError_t e) {
 // Workspace sections, in bytes from the workspace base.
 struct Layout {
   size_t partials = 0;   // Partial[(max_seqs + 2 * max_draft_rows) * tasks_per_row]
-  size_t tiles = 0;      // double[max_seqs * num_tiles]
+  size_t tiles = 0;      // double[max_seqs * num_tiles * kTileTerms]
   size_t counters = 0;   // uint32[max_seqs], cleared by the row pass of each call
   size_t total = 0;
 };
@@ -72,7 +72,7 @@ Layout make_layout(int32_t max_seqs, int64_t max_draft_rows, int64_t tasks_per_r
   L.partials = off;
   off = align_up(off + (size_t)rows * (size_t)tasks_per_row * sizeof(sv::Partial));
   L.tiles = off;
-  off = align_up(off + (size_t)max_seqs * (size_t)num_tiles * sizeof(double));
+  off = align_up(off + (size_t)max_seqs * (size_t)num_tiles * sv::kTileTerms * sizeof(double));
   L.counters = off;
   off = align_up(off + (size_t)max_seqs * sizeof(uint32_t));
   L.total = off < kAlign ? kAlign : off;
@@ -152,7 +152,7 @@ hipError_t launch_sampled(const spec_verify_ctx* ctx, const spec_verify_args* a,
   int64_t G = ctx->cu_count / B;
   if (G > (ctx->num_tiles + 1) / 2) G = (ctx->num_tiles + 1) / 2;
   if (G < 1 || MODE == kDraftPoint) G = 1;
-  const size_t lds = (size_t)ctx->num_tiles * sizeof(double);
+  const size_t lds = (size_t)ctx->num_tiles * kTileTerms * sizeof(double);
   return launch(finish_kernel<DT, VEC, CHECK, MODE>, dim3((unsigned)(B * G)), dim3(kThreads), lds,
                 stream, ev, 1, a->target_logits, draft, a->ld, ctx->vocab, R_t, R_d,
                 a->cu_draft, a->draft_tokens, a->uniforms, ec, (const Partial*)partials,

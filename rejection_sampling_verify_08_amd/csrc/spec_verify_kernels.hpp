@@ -603,8 +603,9 @@ __device__ __forceinline__ RowNorm combine_rows_packed(const Partial* __restrict
   return r;
 }
 
-// Final-draw weights of one group, in a common positive scale:
-//   residual : w = max(0, e_p - rho * e_q) = max(0, p - q) * s_p * 2^Kp
+// Final-draw weights of one group, in a common positive scale (the target
+// row's terms e_p = 2^((l_p - M_p) c + K_p), i.e. p * s_p * 2^Kp):
+//   residual : w = max(0, p - q) * s_p * 2^Kp
 //   point    : w = e_p, except 0 at token x = max(0, p - delta_x) * s_p * 2^Kp
 //   bonus    : w = e_p                      = p * s_p * 2^Kp
 constexpr int kDrawBonus = 0;
@@ -612,26 +613,60 @@ constexpr int kDrawResidual = 1;   // draft distribution given by draft logits
 constexpr int kDrawPoint = 2;      // draft distribution is the point mass at x
 
 struct DrawConsts {
-  float Ap, Aq;          // per-row shifts
-  float rho_hi, rho_lo;  // rho = (s_p / s_q) 2^(Kp - Kq), split
-  float C_hi, C_lo;      // C = (Mq - Mp) c - log2(s_p / s_q), split (fp32 residuals)
+  float Ap;              // target row shift
+  float Aq;              // residual: draft row shift
+  float dK;              // residual: K_p - K_q, moves draft terms into the target's scale
+  float dM;              // residual: M_p - M_q (the two rows' maxima)
+  float g;               // residual: 1 - s_p / s_q (the normaliser ratio, see below)
   int residual;          // kDrawBonus, kDrawResidual or kDrawPoint
   int64_t x;             // kDrawPoint: the rejected draft token
 };
 
-// 1 - 2^-d for d > 0 with a small relative error: below 1/2 the Taylor
-// series of 1 - e^-u in u = d ln 2 (the direct form would cancel), evaluated
-// innermost first and truncated after the u^8 term (relative remainder
-// < 6e-10); exp2 above.
-__device__ __forceinline__ float one_minus_exp2_neg(float d) {
-  if (d < 0.5f) {
-    const float u = d * 0.693147182f;   // ln 2 in float
-    float t = 1.0f;
+// The residual max(0, p - q) without cancellation.  With each row centred on
+// its own maximum, d0_k = ((l_p - l_q) - (M_p - M_q)) c is the log2 ratio of
+// the two rows' centred terms (exactly 0 where the rows agree up to the
+// shift), and q_k / p_k = 2^(-d0_k) s_p / s_q.  Then
+//   p_k - q_k = p_k (m0_k + g (1 - m0_k)),  m0_k = 1 - 2^(-d0_k),  g = 1 - s_p / s_q,
+// linear in g.  The element's terms, in the weights' scale:
+//   r0 = e_p - e_q       (sums to s_p' - s_q', the C-free row difference)
+//   qs = e_q             (q_k in the same scale; dw/dg)
+//   w  = max(0, r0 + g qs)
+// with e_q the draft term moved into the target's scale.  Below |d0| = 1/2
+// r0 = e_p m0 from m0's series (relative precision near 0) and qs = e_p - r0;
+// above it both terms are exponentials and their difference keeps at least
+// 29% of its larger term.  -inf logits need no special case: d0 is then
+// infinite or NaN (the exponential branch) and the exponentials are 0.
+constexpr float kSeriesLimit = 0.5f;
+// 1 - 2^-x = sum_{n>=1} (-1)^(n+1) (x ln 2)^n / n!, highest degree first;
+// truncated after n = 8 (relative remainder < 1e-9 for |x| <= 1/2)
+__constant__ float kOmExp2[8] = {
+    -1.3215486790144305e-06f, 1.5252733804059838e-05f, -1.5403530393381606e-04f,
+    1.3333558146428441e-03f, -9.618129107628477e-03f, 5.5504108664821576e-02f,
+    -2.402265069591007e-01f, 6.931471805599453e-01f};
+
+struct ResidualTerm {
+  float w, wu, r0, qs;   // w = max(0, wu): wu is the weight before the clip
+};
+
+__device__ __forceinline__ ResidualTerm residual_term(float lp, float lq, const DrawConsts& dc,
+                                                      const ExpConsts& ec) {
+  const float ep = exp_term(lp, dc.Ap, ec);
+  float yq = __builtin_fmaf(lq, ec.c_hi, dc.Aq);
+  yq = __builtin_fmaf(lq, ec.c_lo, yq) + dc.dK;
+  const float qx = __builtin_amdgcn_exp2f(yq);
+  // c_hi alone: c_lo / c_hi < 2^-23 is a relative change of d0 below fp32
+  // rounding
+  const float d0 = ((lp - lq) - dc.dM) * ec.c_hi;
+  float ps = kOmExp2[0];
 #pragma unroll
-    for (int n = 8; n >= 2; --n) t = __builtin_fmaf(-u * (1.0f / (float)n), t, 1.0f);
-    return u * t;
-  }
-  return 1.0f - __builtin_amdgcn_exp2f(-d);
+  for (int i = 1; i < 8; ++i) ps = __builtin_fmaf(ps, d0, kOmExp2[i]);
+  const bool small = __builtin_fabsf(d0) < kSeriesLimit;
+  ResidualTerm r;
+  r.r0 = small ? ep * (ps * d0) : ep - qx;
+  r.qs = small ? ep - r.r0 : qx;
+  r.wu = __builtin_fmaf(dc.g, r.qs, r.r0);
+  r.w = __builtin_fmaxf(r.wu, 0.0f);     // a NaN (0 - 0 * inf) gives 0
+  return r;
 }
 
 // rp/rq hold group g of the p and q rows (rq unused unless kDrawResidual);
@@ -651,30 +686,8 @@ __device__ __forceinline__ void weights_of(const GroupRaw<DT>& rp, const GroupRa
   } else if (dc.residual == kDrawResidual) {
     float lq[kGroup];
     unpack<DT>(rq, lq);
-    if constexpr (DT == 0) {
-      // fp32 logits: p - q = p (1 - 2^-d) with d = log2(p/q) =
-      // (l_p - l_q) c + C.  l_p - l_q is exact when the two are close, so a
-      // residual made of small differences keeps its relative precision
-      // (e_p - rho e_q would lose it to cancellation).
 #pragma unroll
-      for (int k = 0; k < kGroup; ++k) {
-        const float ep = exp_term(lp[k], dc.Ap, ec);
-        const float dl = lp[k] - lq[k];
-        float d = __builtin_fmaf(dl, ec.c_hi, dc.C_hi);
-        d = __builtin_fmaf(dl, ec.c_lo, d);
-        d = d + dc.C_lo;
-        w[k] = (ep > 0.0f && d > 0.0f) ? ep * one_minus_exp2_neg(d) : 0.0f;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kGroup; ++k) {
-        const float ep = exp_term(lp[k], dc.Ap, ec);
-        const float eq = exp_term(lq[k], dc.Aq, ec);
-        float d = __builtin_fmaf(-eq, dc.rho_hi, ep);
-        d = __builtin_fmaf(-eq, dc.rho_lo, d);
-        w[k] = d > 0.0f ? d : 0.0f;
-      }
-    }
+    for (int k = 0; k < kGroup; ++k) w[k] = residual_term(lp[k], lq[k], dc, ec).w;
   } else {
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) w[k] = exp_term(lp[k], dc.Ap, ec);
@@ -926,6 +939,67 @@ __device__ __forceinline__ int64_t draw_from_task_sums(
   return block_search<DT>(rp, rp, gi, active, dc, ec, tt, p_excl, ds);
 }
 
+// ---------------------------------------------------------------- residual tiles
+
+constexpr int kTileTerms = 4;                 // W, Q, R0, B per tile
+constexpr double kBand = 0x1p-20;             // |g* - g| / max(1, |g|) the first-order move covers
+constexpr double kCorrectionTol = 0x1p-24;    // band error allowed, relative to W
+constexpr double kResidualFloor = 0x1p-60;    // residual mass the fp32 terms resolve
+
+// The residual tile pass over tiles [t_lo, t_hi) of one row pair, by the
+// calling workgroup: wave w takes tile t_lo + w first, then the next
+// unclaimed tile from the LDS counter *next (cleared by the caller).  Waves
+// progress at different rates (two share a SIMD), and a static round-robin
+// left the last wave of a workgroup ~4.6 us behind its first.  A tile is
+// 2048 logits: 256 consecutive groups, lane l holding groups l, l+64, l+128,
+// l+192 (each 16-byte load instruction covers 1 KB of contiguous logits).
+// For every tile, emit(t, v) is called by all lanes of the wave with the
+// tile's sums v = {W, Q, R0, B} (double, equal in every lane); a tile's sums
+// do not depend on the wave that computes them.
+template <int DT, bool VEC, typename Emit>
+__device__ __forceinline__ void residual_tiles(const void* prow, const void* qrow, int64_t V,
+                                               int64_t t_lo, int64_t t_hi, const DrawConsts& dc,
+                                               const ExpConsts& ec, int* next, Emit emit) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // the band scales with g: g's own rounding error is relative
+  const float band = (float)kBand * __builtin_fmaxf(1.0f, __builtin_fabsf(dc.g));
+  for (int64_t t = t_lo + wave; t < t_hi;) {
+    GroupRaw<DT> cp[kTileGroupsPerLane], cq[kTileGroupsPerLane];
+    load_tile<DT, VEC>(prow, t, V, lane, cp);
+    load_tile<DT, VEC>(qrow, t, V, lane, cq);
+    float sw = 0.0f, sq = 0.0f, sr = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTileGroupsPerLane; ++j) {
+      float lp[kGroup], lq[kGroup];
+      unpack<DT>(cp[j], lp);
+      unpack<DT>(cq[j], lq);
+      float gw = 0.0f, gq = 0.0f, gr = 0.0f, gb = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        const ResidualTerm r = residual_term(lp[k], lq[k], dc, ec);
+        gw += r.w;
+        gr += r.r0;
+        gq += r.wu > 0.0f ? r.qs : 0.0f;
+        gb += __builtin_fabsf(r.wu) <= band * r.qs ? r.qs : 0.0f;
+      }
+      sw += gw;
+      sq += gq;
+      sr += gr;
+      sb += gb;
+    }
+    double v[kTileTerms];
+    v[0] = wave_xor_sum((double)sw);
+    v[1] = wave_xor_sum((double)sq);
+    v[2] = wave_xor_sum((double)sr);
+    v[3] = wave_xor_sum((double)sb);
+    emit(t, v);
+    int claimed = 0;
+    if (lane == 0) claimed = atomicAdd(next, 1);
+    t = t_lo + kWaves + (int64_t)__builtin_amdgcn_readfirstlane(claimed);
+  }
+}
+
 // ---------------------------------------------------------------- finishing
 
 // Draft-distribution modes of the finishing kernel.
@@ -953,7 +1027,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     float* __restrict__ out_p, float* __restrict__ out_q, float* __restrict__ out_residual,
     uint32_t* __restrict__ status) {
   __shared__ SeqShared sh;
-  extern __shared__ double tile_sum[];   // [num_tiles], used when G == 1
+  extern __shared__ double tile_sum[];   // [kTileTerms * num_tiles]: tile sums, task sums
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -1160,28 +1234,18 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
   dc.x = (MODE == kDraftPoint && residual) ? (int64_t)sh.x[n - lo] : -1;
   dc.Ap = shift_of(Mp, ec);
   const double Kp = offset_of(Mp, dc.Ap, ec);
+  const double unit = sp * exp2(Kp);   // the weights' scale: sum of e_p
+  dc.Aq = 0.0f;
+  dc.dK = 0.0f;
+  dc.dM = 0.0f;
+  dc.g = 0.0f;
   if (tile_pass) {
     const float Mq = sh.M[1][n - lo];
     const double sq = sh.s[1][n - lo];
     dc.Aq = shift_of(Mq, ec);
-    const double rho = (sp / sq) * exp2(Kp - offset_of(Mq, dc.Aq, ec));
-    dc.rho_hi = (float)rho;
-    dc.rho_lo = (float)(rho - (double)dc.rho_hi);
-    if constexpr (DT == 0) {   // only the fp32 weights use C
-      const double C = ((double)Mq - (double)Mp) * ((double)ec.c_hi + (double)ec.c_lo) -
-                       log2(sp / sq);
-      dc.C_hi = (float)C;
-      dc.C_lo = (float)(C - (double)dc.C_hi);
-    } else {
-      dc.C_hi = 0.0f;
-      dc.C_lo = 0.0f;
-    }
-  } else {
-    dc.Aq = 0.0f;
-    dc.rho_hi = 0.0f;
-    dc.rho_lo = 0.0f;
-    dc.C_hi = 0.0f;
-    dc.C_lo = 0.0f;
+    dc.dK = (float)(Kp - offset_of(Mq, dc.Aq, ec));
+    dc.dM = Mp - Mq;
+    dc.g = (float)((sq - sp) / sq);    // 1 - s_p / s_q from the row pass
   }
   __shared__ DrawShared ds;
   uint32_t fbad = sh.bad;
@@ -1193,42 +1257,41 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     token = draw_from_task_sums<DT, VEC>(part + (prow_t0 + n) * tpr, tpr, prow, V, dc, ec,
                                          u_final, tile_sum, ds, fbad, total);
   } else {
-    // ---- tile sums of this workgroup's share of the tiles.  A tile is 2048
-    // logits: 256 consecutive groups, lane l holding groups l, l+64, l+128,
-    // l+192 (each 16-byte load instruction covers 1 KB of contiguous logits).
-    // Wave w takes tile t_lo + w first, then the next unclaimed tile from an
-    // LDS counter: waves progress at different rates (two share a SIMD), and
-    // a static round-robin left the last wave of a workgroup ~4.6 us behind
-    // its first.  A tile's sum does not depend on the wave that computes it.
-    const int64_t per = (num_tiles + G - 1) / G;
+    // ---- the residual's tile pass.  Tile sums of this workgroup's share:
+    // per tile the weights W (with the row pass's g), the draft terms Q over
+    // the support (dW/dg), the C-free difference R0 and the band mass B of
+    // elements within 2^-20 of the support's edge.  Sums of a lane's 32
+    // elements are fp32, the wave's total is double.  Tile arrays, in LDS:
+    // W at tile_sum[0, nt), Q at [nt, 2 nt), R0 at [2 nt, 3 nt), B at
+    // [3 nt, 4 nt).
+    const int64_t nt = num_tiles;
+    const int64_t per = (nt + G - 1) / G;
     const int64_t t_lo = (int64_t)g * per;
-    const int64_t t_hi = t_lo + per < num_tiles ? t_lo + per : num_tiles;
-    double* ts_seq = tile_sums + b * num_tiles;
-    for (int64_t t = t_lo + wave; t < t_hi;) {
-      GroupRaw<DT> cp[kTileGroupsPerLane], cq[kTileGroupsPerLane];
-      load_tile<DT, VEC>(prow, t, V, lane, cp);
-      load_tile<DT, VEC>(qrow, t, V, lane, cq);
-      float lsum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kTileGroupsPerLane; ++j) {
-        float w[kGroup];
-        weights_of<DT>(cp[j], cq[j], (t * kTileGroups + j * 64 + lane) * kGroup, dc, ec, w);
-        lsum += seq_sum8(w);
+    const int64_t t_hi = t_lo + per < nt ? t_lo + per : nt;
+    double* ts_seq = tile_sums + b * nt * kTileTerms;
+    residual_tiles<DT, VEC>(prow, qrow, V, t_lo, t_hi, dc, ec, &sh.tile_next,
+                            [&](int64_t t, const double v[kTileTerms]) {
+      // lane k < 4 stores term k (selected, not indexed: v stays in registers)
+      const double vk = lane == 0 ? v[0] : lane == 1 ? v[1] : lane == 2 ? v[2] : v[3];
+      if (lane < kTileTerms) {
+        if (G == 1) tile_sum[lane * nt + t] = vk;
+        else __hip_atomic_store(&ts_seq[t * kTileTerms + lane], vk, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
       }
-      const double ts = wave_xor_sum((double)lsum);
-      int claimed = 0;
-      if (lane == 0) {
-        if (G == 1) tile_sum[t] = ts;
-        else __hip_atomic_store(&ts_seq[t], ts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        claimed = atomicAdd(&sh.tile_next, 1);
-      }
-      t = t_lo + kWaves + (int64_t)__builtin_amdgcn_readfirstlane(claimed);
-    }
+    });
     // ---- arrival: with G > 1 the tile sums cross workgroups.  They were
-    // written with agent-scope atomic stores (through to the device-coherent
-    // level); each wave waits for their acknowledgement before the barrier,
-    // then one thread counts the workgroup in.  The last of the G workgroups
-    // reads them back with agent-scope atomic loads.
+    // written with agent-scope atomic stores, which on gfx950 write through
+    // the XCD's L2 to the device-coherent level; each wave waits for their
+    // acknowledgement (s_waitcnt) before the barrier, then one thread counts
+    // the workgroup in with a relaxed agent-scope atomic add, which is
+    // issued only after every store of the workgroup is acknowledged.  The
+    // last of the G workgroups sees the count G - 1 and only then issues
+    // agent-scope atomic loads, which read the device-coherent level rather
+    // than its own L2.  This relies on that gfx950 behaviour (stores
+    // acknowledged at the coherent level before the count, loads issued
+    // after the count returns) instead of an agent-scope release / acquire
+    // pair, whose L2 write-back and invalidate made the kernel several
+    // times slower with hundreds of workgroups.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1241,19 +1304,60 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
       __syncthreads();
       if (!ds.last_wg) return;
       // the last workgroup copies the tile sums into its LDS
-      for (int64_t t = tid; t < num_tiles; t += kThreads)
-        tile_sum[t] = __hip_atomic_load(&ts_seq[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int64_t i = tid; i < nt * kTileTerms; i += kThreads) {
+        const int64_t t = i / kTileTerms, k = i - t * kTileTerms;
+        tile_sum[k * nt + t] =
+            __hip_atomic_load(&ts_seq[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       __syncthreads();
     }
+    // ---- the exact normaliser ratio.  R0 = s_p' - s_q' (both in the
+    // weights' scale) comes from per-element differences, so it is exact to
+    // the rounding of those differences, while the row pass's s_p / s_q is
+    // exact only to its sums' rounding (~1e-8): g* = 1 - s_p' / s_q' =
+    // -R0 / (s_p' - R0).  W is linear in g for a fixed support, so the tile
+    // sums move by (g* - g) Q; elements whose sign can change lie in the
+    // band (g* - g is checked to be inside it), and their mass bounds the
+    // error.  Waves 0-3 total the four arrays in a fixed order.
+    if (wave < kTileTerms) {
+      const double tot = wave_total(tile_sum + wave * nt, nt, lane);
+      if (lane == 0) ds.red[wave] = tot;
+    }
+    __syncthreads();
+    const double R0 = ds.red[2];
+    const float g_star = (float)(-R0 / (unit - R0));
+    const double dg = (double)g_star - (double)dc.g;
+    const double w_star = ds.red[0] + dg * ds.red[1];
+    const double band = kBand * __builtin_fmax(1.0, __builtin_fabs((double)dc.g));
+    const bool linear_ok = w_star > 0.0 && __builtin_fabs(dg) <= band &&
+                           2.0 * __builtin_fabs(dg) * ds.red[3] <= kCorrectionTol * w_star;
+    dc.g = g_star;                     // the search below uses g*
+    __syncthreads();                   // ds.red is reused
+    if (linear_ok) {
+      for (int64_t t = tid; t < nt; t += kThreads) {
+        const double c = tile_sum[t] + dg * tile_sum[nt + t];
+        tile_sum[t] = c > 0.0 ? c : 0.0;
+      }
+    } else {
+      // the support moves with g: this workgroup passes over both rows again
+      // with g* (rare: rows that agree to the row pass's rounding)
+      if (tid == 0) sh.tile_next = 0;
+      __syncthreads();
+      residual_tiles<DT, VEC>(prow, qrow, V, 0, nt, dc, ec, &sh.tile_next,
+                              [&](int64_t t, const double v[kTileTerms]) {
+        if (lane == 0) tile_sum[t] = v[0];
+      });
+    }
+    __syncthreads();
     // ---- wave 0 scans the tile sums in order and finds the tile holding
     // t = u * S; an empty residual (invalid input or extreme rounding) falls
     // back to a draw from p_n through the task sums.
     if (wave == 0) {
       double tt = 0.0;
-      total = wave_total(tile_sum, num_tiles, lane);
+      total = wave_total(tile_sum, nt, lane);
       if (total > 0.0) {
         tt = (double)u_final * total;
-        find_interval(tile_sum, num_tiles, tt, lane, ds);
+        find_interval(tile_sum, nt, tt, lane, ds);
       }
       if (lane == 0) {
         ds.total = total;
@@ -1271,6 +1375,9 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
       token = draw_from_task_sums<DT, VEC>(part + (prow_t0 + n) * tpr, tpr, prow, V, dd, ec,
                                            u_final, tile_sum, ds, fbad, ptotal);
     } else {
+      // below 2^-60 of the unit mass, underflowed fp32 terms (< 2^-126 each)
+      // could be a measurable share of the residual
+      if (total < kResidualFloor * unit) fbad |= SPEC_VERIFY_DEV_RESIDUAL_UNRESOLVED;
       // ---- re-scan tile tau: thread t < 256 holds group tau*256 + t
       const int64_t tau = ds.tau;
       GroupRaw<DT> rp, rq;
@@ -1287,7 +1394,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     out_tokens[trow0 + n] = (int32_t)token;
     if (out_residual)
       out_residual[b] = (residual && !(fbad & SPEC_VERIFY_DEV_EMPTY_RESIDUAL))
-                            ? (float)(total * exp2(-Kp) / sp)
+                            ? (float)(total / unit)
                             : 0.0f;
     status_or(status, fbad);
   }

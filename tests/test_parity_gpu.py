@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import compare, log, make_verifier, run_gpu, to_device
+from tests.gpu_helpers import compare, log, make_verifier, run_gpu, status_ok, ties, to_device
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -168,20 +168,21 @@ def _masked_low_temperature_case(seed):
 
 
 @pytest.mark.parametrize("seed", [149, 694, 1151])
-def test_residual_below_fp32_resolution(seed):
-    """Rejections whose residual mass is below 2^-20 (p and q near-identical
-    one-hot distributions at T ~ 0.05): the oracle flags them (bit 3), the
-    draw there is only required to be a valid token, the residual sum is not
-    compared, and the kernel may report an empty residual (status bit 6)."""
+def test_masked_near_equal_residuals(seed):
+    """Masked rows at low temperature whose rejections leave residuals of
+    near-equal distributions (p and q one-hot-like on the same token; S from
+    ~1e-15 to ~1e-8): every residual the oracle resolves (E below the tie
+    window) must give the oracle's token, including seed 694's S = 6.7e-9
+    draw; where S is at the double rounding of the normalisers (E ~ 1) the
+    token must have a weight the oracle's bound does not exclude."""
     inp = _masked_low_temperature_case(seed)
-    label = f"residual below fp32 resolution, seed {seed}"
+    label = f"masked near-equal residuals, seed {seed}"
     log(f"[case] {label}: B={inp.num_seqs} V={inp.vocab} {inp.dtype} T={inp.temperature:.4f}")
     ora = oracle.verify_inputs(inp)
-    flags = np.asarray(ora.flagged)
-    assert (flags & 8).any()
+    assert (np.asarray(ora.flagged) & 8).any()
     gpu = run_gpu(inp)
     compare(inp, gpu, ora, label=label)
-    assert gpu.status == 0 or (gpu.status == 64 and (flags & 12).any()), hex(gpu.status)
+    assert status_ok(gpu.status, ora), hex(gpu.status)
 
 
 def test_identical_rows_always_accepted():
@@ -338,7 +339,7 @@ def test_lossless_on_gpu_one_launch():
             z = (passed - reached * a) / np.sqrt(reached * a * (1 - a))
             assert abs(z) < stats.norm.isf(alpha_level / 2), (i, z)
     ora = oracle.verify_inputs(inp)
-    flagged = ora.flagged != 0
+    flagged = ties(ora.flagged)
     same = (gpu.num_accepted == ora.num_accepted) & \
         (out == ora.out_tokens.reshape(N, g + 1)).all(axis=1)
     log(f"[parity] lossless one launch: seqs={N} flagged={int(flagged.sum())} "
