@@ -187,10 +187,10 @@ SPEC_VERIFY_API int spec_verify_create(spec_verify_ctx **out, int device,
  * Workspace bytes a context with these bounds needs, without creating one or
  * touching the HIP runtime (host-only; lets a caller size its allocation
  * first).  The workspace holds one 16-byte row-statistics partial per 4096
- * logits of every target and draft row (R_t + R_d = B + 2 R_d rows), one
- * double per 2048-logit tile of each sequence's final-draw row, and one
- * arrival counter per sequence (cleared inside every call).  Returns OK,
- * EINVAL or EUNSUPPORTED.
+ * logits of every target and draft row (R_t + R_d = B + 2 R_d rows), four
+ * doubles per 2048-logit tile of each sequence's final-draw rows (the
+ * residual's tile sums), and one arrival counter per sequence (cleared
+ * inside every call).  Returns OK, EINVAL or EUNSUPPORTED.
  */
 SPEC_VERIFY_API int spec_verify_query_workspace(int64_t vocab, int32_t max_seqs,
                                                 int64_t max_draft_rows,
