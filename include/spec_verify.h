@@ -216,6 +216,30 @@ SPEC_VERIFY_API int spec_verify_run(const spec_verify_ctx *ctx,
                                     const spec_verify_args *args,
                                     void *hip_stream);
 
+/* Size of the library's own workspace used by spec_verify_run_static. */
+#define SPEC_VERIFY_STATIC_WORKSPACE_BYTES (16u << 20)
+
+/*
+ * spec_verify_run without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The workspace is the library's own
+ * file-scope device array of SPEC_VERIFY_STATIC_WORKSPACE_BYTES (16 MiB),
+ * one copy per device the library runs on, held until the process ends; its
+ * device address is resolved once per device by spec_verify_create.
+ * args->workspace and args->workspace_bytes are ignored; nothing is
+ * allocated or freed.  The call's own need, spec_verify_query_workspace(V,
+ * B, R_d) for this call's B and R_d, must fit in the array: otherwise it
+ * returns SPEC_VERIFY_ECAPACITY and enqueues nothing (16 MiB holds, e.g.,
+ * 1024 sequences of 8 drafts at V = 128256, which need 10.5 MiB).  Every call on one device
+ * shares the array and each call clears the state it needs itself, so calls
+ * ordered on one stream are safe; calls that can overlap on one device
+ * (different streams, or graphs replayed concurrently) race and must not be
+ * issued.  Same kernels, results and other errors as spec_verify_run.
+ */
+SPEC_VERIFY_API int spec_verify_run_static(const spec_verify_ctx *ctx,
+                                           const spec_verify_args *args,
+                                           void *hip_stream);
+
 /*
  * Greedy verification: the temperature -> 0 limit of spec_verify_run.
  * [B] item 流程编排: the drafts are compared in order with the target's

@@ -31,7 +31,7 @@ MAX_TREE_NODES, MAX_TREE_CHILDREN = 1024, 64
 
 EXPORTED = ("spec_verify_create", "spec_verify_query_workspace",
             "spec_verify_workspace_size",
-            "spec_verify_num_kernels", "spec_verify_run",
+            "spec_verify_num_kernels", "spec_verify_run", "spec_verify_run_static",
             "spec_verify_run_greedy", "spec_verify_run_point_drafts",
             "spec_verify_tree_run_greedy", "spec_verify_tree_run_point",
             "spec_verify_destroy", "spec_verify_status_string",
@@ -143,7 +143,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_workspace_size.argtypes = [P]
     lib.spec_verify_num_kernels.restype = ctypes.c_int
     lib.spec_verify_num_kernels.argtypes = [P]
-    for name in ("spec_verify_run", "spec_verify_run_greedy", "spec_verify_run_point_drafts"):
+    for name in ("spec_verify_run", "spec_verify_run_static", "spec_verify_run_greedy",
+                 "spec_verify_run_point_drafts"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P, ctypes.POINTER(Args), P]
@@ -276,6 +277,17 @@ class SpecVerifier:
                          draft_tokens, uniforms, temperature, num_seqs, total_draft_rows,
                          out, timing_events, stream)
 
+    def run_static(self, cu_draft, target_logits, draft_logits, draft_tokens, uniforms,
+                   temperature: float, *, num_seqs: Optional[int] = None,
+                   total_draft_rows: Optional[int] = None, out: Optional[VerifyOutput] = None,
+                   stream=None) -> VerifyOutput:
+        """spec_verify_run_static: the same verify step with the library's
+        own device workspace (no workspace argument, nothing allocated by
+        the library; `out` is still the caller's)."""
+        return self._run("spec_verify_run_static", cu_draft, target_logits, draft_logits,
+                         draft_tokens, uniforms, temperature, num_seqs, total_draft_rows,
+                         out, None, stream)
+
     def point_drafts(self, cu_draft, target_logits, draft_tokens, uniforms,
                      temperature: float, *, num_seqs: Optional[int] = None,
                      out: Optional[VerifyOutput] = None,
@@ -368,6 +380,7 @@ class SpecVerifier:
                             ("uniforms", uniforms, torch.float32)):
             if t is not None and (t.dtype != dt or not t.is_contiguous()):
                 raise ValueError(f"{name} must be a contiguous {dt} tensor")
+        static = entry == "spec_verify_run_static"   # the library's own workspace
         events = None
         if timing_events is not None:
             arr = (ctypes.c_void_p * len(timing_events))(
@@ -382,8 +395,9 @@ class SpecVerifier:
             uniforms=_ptr(uniforms), temperature=float(temperature),
             out_tokens=_ptr(out.out_tokens), out_num_accepted=_ptr(out.num_accepted),
             out_p_draft=_ptr(out.p_draft), out_q_draft=_ptr(out.q_draft),
-            out_residual_sum=_ptr(out.residual_sum), workspace=_ptr(self.workspace),
-            workspace_bytes=int(self.workspace.numel()), status=_ptr(out.status),
+            out_residual_sum=_ptr(out.residual_sum),
+            workspace=None if static else _ptr(self.workspace),
+            workspace_bytes=0 if static else int(self.workspace.numel()), status=_ptr(out.status),
             timing_events=ctypes.cast(events, ctypes.c_void_p) if events is not None else None)
         if stream is None:
             stream = torch.cuda.current_stream(self.device)

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "spec_verify.h"
@@ -21,6 +22,14 @@
 
 static_assert(sv::kMaxTreeNodes == SPEC_VERIFY_MAX_TREE_NODES, "tree node limit");
 static_assert(sv::kMaxChildren == SPEC_VERIFY_MAX_TREE_CHILDREN, "tree child limit");
+
+// The workspace of spec_verify_run_static: a file-scope device array, one
+// copy per device the library runs on, held until the process ends.  In
+// host code its name is only a stand-in for the symbol, never a device
+// address: the address comes from hipGetSymbolAddress, resolved once per
+// device by spec_verify_create (resolve_scratch below), and only that
+// address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SPEC_VERIFY_STATIC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -49,6 +58,7 @@ struct Layout {
 
 struct spec_verify_ctx {
   int device;
+  void* scratch;           // device address of `scratch` on this device
   int64_t vocab;
   int dtype;
   int32_t max_seqs;
@@ -77,6 +87,34 @@ Layout make_layout(int32_t max_seqs, int64_t max_draft_rows, int64_t tasks_per_r
   off = align_up(off + (size_t)max_seqs * sizeof(uint32_t));
   L.total = off < kAlign ? kAlign : off;
   return L;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices];   // per device: the address of `scratch`, once resolved
+
+// The device address of `scratch` on `device`, resolved on the first call
+// for that device with the device made current (the caller's current device
+// is restored).
+hipError_t resolve_scratch(int device, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!g_scratch[device]) {
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e != hipSuccess) return e;
+    if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (prev != device) {
+      const hipError_t r = hipSetDevice(prev);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch[device] = ptr;
+  }
+  *out = g_scratch[device];
+  return hipSuccess;
 }
 
 // log2(e)/T split into a float rounded down and a positive float remainder.
@@ -121,7 +159,7 @@ hipError_t launch(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t strea
 
 template <int DT, bool VEC, bool CHECK, int MODE>
 hipError_t launch_sampled(const spec_verify_ctx* ctx, const spec_verify_args* a,
-                          hipStream_t stream) {
+                          const Layout& layout, hipStream_t stream) {
   using namespace sv;
   const int64_t B = a->num_seqs;
   const int64_t R_d = a->total_draft_rows;
@@ -131,9 +169,9 @@ hipError_t launch_sampled(const spec_verify_ctx* ctx, const spec_verify_args* a,
   const void* draft = MODE == kDraftLogits ? a->draft_logits : nullptr;
   const ExpConsts ec = exp_consts(a->temperature);
   char* ws = static_cast<char*>(a->workspace);
-  Partial* partials = reinterpret_cast<Partial*>(ws + ctx->layout.partials);
-  double* tiles = reinterpret_cast<double*>(ws + ctx->layout.tiles);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + ctx->layout.counters);
+  Partial* partials = reinterpret_cast<Partial*>(ws + layout.partials);
+  double* tiles = reinterpret_cast<double*>(ws + layout.tiles);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + layout.counters);
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(a->timing_events);
   hipError_t e;
 
@@ -163,14 +201,14 @@ hipError_t launch_sampled(const spec_verify_ctx* ctx, const spec_verify_args* a,
 
 template <int DT, bool VEC, bool CHECK>
 hipError_t launch_greedy(const spec_verify_ctx* ctx, const spec_verify_args* a,
-                         hipStream_t stream) {
+                         const Layout& layout, hipStream_t stream) {
   using namespace sv;
   const int64_t B = a->num_seqs;
   const int64_t R_d = a->total_draft_rows;
   const int64_t R_t = R_d + B;
   // the argmax partials reuse the row-statistics section of the workspace
   ArgPartial* partials =
-      reinterpret_cast<ArgPartial*>(static_cast<char*>(a->workspace) + ctx->layout.partials);
+      reinterpret_cast<ArgPartial*>(static_cast<char*>(a->workspace) + layout.partials);
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(a->timing_events);
   hipError_t e;
   const int64_t grid1 = ceil_div(R_t * ctx->tasks_per_row, kStatsWaves);
@@ -185,22 +223,22 @@ hipError_t launch_greedy(const spec_verify_ctx* ctx, const spec_verify_args* a,
 }
 
 template <int DT, bool VEC, bool CHECK>
-hipError_t launch_mode(const spec_verify_ctx* ctx, const spec_verify_args* a, hipStream_t s,
-                       Mode mode) {
+hipError_t launch_mode(const spec_verify_ctx* ctx, const spec_verify_args* a, const Layout& L,
+                       hipStream_t s, Mode mode) {
   switch (mode) {
-    case Mode::kSampled: return launch_sampled<DT, VEC, CHECK, sv::kDraftLogits>(ctx, a, s);
-    case Mode::kPointDrafts: return launch_sampled<DT, VEC, CHECK, sv::kDraftPoint>(ctx, a, s);
-    default: return launch_greedy<DT, VEC, CHECK>(ctx, a, s);
+    case Mode::kSampled: return launch_sampled<DT, VEC, CHECK, sv::kDraftLogits>(ctx, a, L, s);
+    case Mode::kPointDrafts: return launch_sampled<DT, VEC, CHECK, sv::kDraftPoint>(ctx, a, L, s);
+    default: return launch_greedy<DT, VEC, CHECK>(ctx, a, L, s);
   }
 }
 
 template <int DT>
-hipError_t dispatch_vec(const spec_verify_ctx* ctx, const spec_verify_args* a,
+hipError_t dispatch_vec(const spec_verify_ctx* ctx, const spec_verify_args* a, const Layout& L,
                         hipStream_t s, bool vec, bool check, Mode mode) {
-  if (vec) return check ? launch_mode<DT, true, true>(ctx, a, s, mode)
-                        : launch_mode<DT, true, false>(ctx, a, s, mode);
-  return check ? launch_mode<DT, false, true>(ctx, a, s, mode)
-               : launch_mode<DT, false, false>(ctx, a, s, mode);
+  if (vec) return check ? launch_mode<DT, true, true>(ctx, a, L, s, mode)
+                        : launch_mode<DT, true, false>(ctx, a, L, s, mode);
+  return check ? launch_mode<DT, false, true>(ctx, a, L, s, mode)
+               : launch_mode<DT, false, false>(ctx, a, L, s, mode);
 }
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -216,10 +254,12 @@ bool grids_fit(const spec_verify_ctx* ctx, int64_t rows, int64_t B) {
   return B <= limit / sv::kThreads / G;
 }
 
-// Host-side argument checks shared by the three entry points, then the
-// launches.  Fields a mode does not use are not checked.
+// Host-side argument checks shared by the entry points, then the launches.
+// Fields a mode does not use are not checked.  With use_scratch the
+// workspace is the library's `scratch` array (args->workspace and
+// workspace_bytes are ignored), laid out for this call's B and R_d.
 int run_mode(const spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_stream,
-             Mode mode) {
+             Mode mode, bool use_scratch = false) {
   if (!ctx || !a) return SPEC_VERIFY_EINVAL;
   const bool sampled = mode != Mode::kGreedy;
   const bool draft_rows = mode == Mode::kSampled;
@@ -231,10 +271,19 @@ int run_mode(const spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_st
   if (a->ld < ctx->vocab) return SPEC_VERIFY_EINVAL;
   if (B > ctx->max_seqs || R_d > ctx->max_draft_rows) return SPEC_VERIFY_ECAPACITY;
   if (!grids_fit(ctx, 2 * R_d + B, B)) return SPEC_VERIFY_ECAPACITY;
+  Layout layout = ctx->layout;
+  void* workspace = a->workspace;
+  size_t workspace_bytes = a->workspace_bytes;
+  if (use_scratch) {
+    layout = make_layout((int32_t)B, R_d, ctx->tasks_per_row, ctx->num_tiles);
+    if (layout.total > SPEC_VERIFY_STATIC_WORKSPACE_BYTES) return SPEC_VERIFY_ECAPACITY;
+    workspace = ctx->scratch;
+    workspace_bytes = SPEC_VERIFY_STATIC_WORKSPACE_BYTES;
+  }
   if (B == 0) return SPEC_VERIFY_OK;
   const size_t esize = ctx->dtype == SPEC_VERIFY_BF16 ? 2 : 4;
   if (!a->cu_draft || !a->target_logits || !a->out_tokens || !a->out_num_accepted ||
-      !a->workspace)
+      !workspace)
     return SPEC_VERIFY_EINVAL;
   if (sampled && !a->uniforms) return SPEC_VERIFY_EINVAL;
   if (R_d > 0 && !a->draft_tokens) return SPEC_VERIFY_EINVAL;
@@ -243,20 +292,23 @@ int run_mode(const spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_st
   if (!aligned(a->target_logits, esize) || (draft && !aligned(draft, esize)) ||
       !aligned(a->cu_draft, 4) || (sampled && !aligned(a->uniforms, 4)) ||
       !aligned(a->out_tokens, 4) || !aligned(a->out_num_accepted, 4) ||
-      !aligned(a->workspace, kAlign))
+      !aligned(workspace, kAlign))
     return SPEC_VERIFY_EINVAL;
-  if (a->workspace_bytes < ctx->layout.total) return SPEC_VERIFY_ECAPACITY;
+  if (workspace_bytes < layout.total) return SPEC_VERIFY_ECAPACITY;
   int cur = -1;
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e);
   if (cur != ctx->device) return SPEC_VERIFY_EINVAL;
 
+  spec_verify_args args = *a;
+  args.workspace = workspace;
+  args.workspace_bytes = workspace_bytes;
   const bool vec = aligned(a->target_logits, 16) && (R_d == 0 || !draft || aligned(draft, 16)) &&
                    ((size_t)a->ld * esize) % 16 == 0;
   const bool check = (ctx->flags & SPEC_VERIFY_FLAG_CHECK) != 0;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  e = ctx->dtype == SPEC_VERIFY_BF16 ? dispatch_vec<1>(ctx, a, s, vec, check, mode)
-                                     : dispatch_vec<0>(ctx, a, s, vec, check, mode);
+  e = ctx->dtype == SPEC_VERIFY_BF16 ? dispatch_vec<1>(ctx, &args, layout, s, vec, check, mode)
+                                     : dispatch_vec<0>(ctx, &args, layout, s, vec, check, mode);
   if (e != hipSuccess) return hip_fail(e);
   return SPEC_VERIFY_OK;
 }
@@ -377,9 +429,13 @@ int spec_verify_create(spec_verify_ctx** out, int device, int64_t vocab, int dty
   int cus = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return hip_fail(e);
+  void* scratch_ptr = nullptr;
+  e = resolve_scratch(device, &scratch_ptr);
+  if (e != hipSuccess) return hip_fail(e);
   spec_verify_ctx* c = new (std::nothrow) spec_verify_ctx();
   if (!c) return SPEC_VERIFY_EINVAL;
   c->device = device;
+  c->scratch = scratch_ptr;
   c->vocab = vocab;
   c->dtype = dtype;
   c->max_seqs = max_seqs;
@@ -413,6 +469,11 @@ int spec_verify_num_kernels(const spec_verify_ctx* ctx) { return ctx ? 2 : 0; }
 
 int spec_verify_run(const spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_stream) {
   return run_mode(ctx, a, hip_stream, Mode::kSampled);
+}
+
+int spec_verify_run_static(const spec_verify_ctx* ctx, const spec_verify_args* a,
+                           void* hip_stream) {
+  return run_mode(ctx, a, hip_stream, Mode::kSampled, true);
 }
 
 int spec_verify_run_point_drafts(const spec_verify_ctx* ctx, const spec_verify_args* a,

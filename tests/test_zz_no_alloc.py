@@ -1,0 +1,72 @@
+"""spec_verify_run_static (the library's file-scope device workspace, no
+allocation) against spec_verify_run (the caller's workspace) on the same
+inputs: two calls in a row on one context, the second with a smaller batch,
+so the second runs over whatever the first left in the shared array.  The
+kernels are the same and the workspace is cleared where it must be, so
+every output must be bit-identical.  A batch whose workspace exceeds the
+array is refused with SPEC_VERIFY_ECAPACITY before anything is enqueued."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests.gpu_helpers import log, to_device
+
+pytestmark = pytest.mark.gpu
+
+FIELDS = ("out_tokens", "num_accepted", "p_draft", "q_draft", "residual_sum", "status")
+
+
+def _host(out):
+    return {k: getattr(out, k).cpu().numpy().copy() for k in FIELDS}
+
+
+def _both(sv, inp):
+    import torch
+    d = to_device(inp)
+    kw = dict(num_seqs=inp.num_seqs, total_draft_rows=inp.draft_rows)
+    ref = sv(d.cu, d.target, d.draft, d.tokens, d.uniforms, inp.temperature, **kw)
+    got = sv.run_static(d.cu, d.target, d.draft, d.tokens, d.uniforms, inp.temperature, **kw)
+    torch.cuda.synchronize()
+    return _host(ref), _host(got)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_static_workspace_matches_caller_workspace(dtype):
+    import torch
+    from rejection_sampling_verify_08_amd import SpecVerifier
+    V = 128256
+    big = W.build("static big", 4100, [8] * 96 + [3, 0, 5, 1] * 8, V, dtype, 1.0,
+                  W.boosted_random_ids_rows(3.0, 20, 8.0), 1.0935)
+    small = W.build("static small", 4101, [2, 7, 0, 4, 1], V, dtype, 0.8,
+                    W.boosted_top_rows(2.0, 5, 4.0), 1.0)
+    sv = SpecVerifier(V, dtype, max_seqs=big.num_seqs, max_draft_rows=big.draft_rows)
+    for inp in (big, small):
+        log(f"[static] {dtype} B={inp.num_seqs} R_d={inp.draft_rows} V={V}")
+        ref, got = _both(sv, inp)
+        assert ref["status"][0] == 0
+        for k in FIELDS:
+            np.testing.assert_array_equal(got[k], ref[k], err_msg=f"{inp.name}: {k}")
+        assert (ref["num_accepted"] >= 0).all()
+    torch.cuda.synchronize()
+
+
+def test_static_workspace_capacity_error():
+    from rejection_sampling_verify_08_amd import binding
+    from rejection_sampling_verify_08_amd import SpecVerifier
+    lib = binding.load_library()
+    V, B, R_d = 128256, 2048, 2048 * 8
+    need = ctypes.c_size_t()
+    assert lib.spec_verify_query_workspace(V, B, R_d, ctypes.byref(need)) == binding.OK
+    assert need.value > 16 << 20
+    log(f"[static] capacity B={B} R_d={R_d} needs {need.value} bytes")
+    sv = SpecVerifier(V, "bf16", max_seqs=B, max_draft_rows=R_d)
+    a = binding.Args(num_seqs=B, total_draft_rows=R_d, ld=V, temperature=1.0)
+    st = lib.spec_verify_run_static(sv._ctx, ctypes.byref(a), None)
+    assert st == binding.ECAPACITY
+    # the same call with the caller's workspace gets past the size check and
+    # stops at the missing pointers instead
+    a.workspace = ctypes.c_void_p(sv.workspace.data_ptr())
+    a.workspace_bytes = sv.workspace.numel()
+    assert lib.spec_verify_run(sv._ctx, ctypes.byref(a), None) == binding.EINVAL
