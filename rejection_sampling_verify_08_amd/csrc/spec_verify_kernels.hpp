@@ -632,17 +632,19 @@ struct DrawConsts {
 //   qs = e_q             (q_k in the same scale; dw/dg)
 //   w  = max(0, r0 + g qs)
 // with e_q the draft term moved into the target's scale.  Below |d0| = 1/2
-// r0 = e_p m0 from m0's series (relative precision near 0) and qs = e_p - r0;
+// r0 = e_p m0 from a polynomial in d0 (relative precision near 0) and qs = e_p - r0;
 // above it both terms are exponentials and their difference keeps at least
 // 29% of its larger term.  -inf logits need no special case: d0 is then
 // infinite or NaN (the exponential branch) and the exponentials are 0.
 constexpr float kSeriesLimit = 0.5f;
-// 1 - 2^-x = sum_{n>=1} (-1)^(n+1) (x ln 2)^n / n!, highest degree first;
-// truncated after n = 8 (relative remainder < 1e-9 for |x| <= 1/2)
-__constant__ float kOmExp2[8] = {
-    -1.3215486790144305e-06f, 1.5252733804059838e-05f, -1.5403530393381606e-04f,
-    1.3333558146428441e-03f, -9.618129107628477e-03f, 5.5504108664821576e-02f,
-    -2.402265069591007e-01f, 6.931471805599453e-01f};
+// (1 - 2^-x) / x on |x| <= 1/2: the degree-5 polynomial that interpolates it
+// at the 6 Chebyshev nodes of [-1/2, 1/2] (coefficients computed in 40-digit
+// arithmetic, highest degree first; relative error of the polynomial below
+// 1.3e-8 on the interval, of its fp32 Horner evaluation below 7.1e-8)
+constexpr int kOmTerms = 6;
+__constant__ float kOmExp2[kOmTerms] = {
+    -1.5453163359779865e-04f, 1.3390863314270973e-03f, -9.618083015084267e-03f,
+    5.5503569543361664e-02f, -2.4022650718688965e-01f, 6.931471824645996e-01f};
 
 struct ResidualTerm {
   float w, wu, r0, qs;   // w = max(0, wu): wu is the weight before the clip
@@ -659,7 +661,7 @@ __device__ __forceinline__ ResidualTerm residual_term(float lp, float lq, const 
   const float d0 = ((lp - lq) - dc.dM) * ec.c_hi;
   float ps = kOmExp2[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) ps = __builtin_fmaf(ps, d0, kOmExp2[i]);
+  for (int i = 1; i < kOmTerms; ++i) ps = __builtin_fmaf(ps, d0, kOmExp2[i]);
   const bool small = __builtin_fabsf(d0) < kSeriesLimit;
   ResidualTerm r;
   r.r0 = small ? ep * (ps * d0) : ep - qx;
