@@ -436,13 +436,18 @@ __device__ __forceinline__ double exp2_accurate(double y) {
 // two near-equal distributions: float terms (one rounding of y_k, ~3e-8 per
 // exponential) left its sum up to ~2.4e-5 off.  bf16 logits keep the float
 // terms (their residual tolerance is 2e-3).
-template <int DT, bool CHECK>
+template <int DT, bool CHECK, bool RAGGED>
 __device__ __forceinline__ void task_stats(const GroupRaw<DT> raw[kTaskGroupsPerLane],
-                                           const ExpConsts& ec, float& m_out, double& s_out,
-                                           uint32_t& bad) {
+                                           const ExpConsts& ec, int64_t valid, float& m_out,
+                                           double& s_out, uint32_t& bad) {
+  // RAGGED: the task ends past the row (its last task, or a row shorter
+  // than one task), with `valid` logits inside it.  Load j covers task
+  // logits [512 j, 512 j + 512); past the row they are -inf, which leaves
+  // the maximum and the sum unchanged, so such loads are skipped.
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kTaskGroupsPerLane; ++j) {
+    if (RAGGED && j * 64 * kGroup >= valid) break;
     float v[kGroup];
     unpack<DT>(raw[j], v);
 #pragma unroll
@@ -458,6 +463,7 @@ __device__ __forceinline__ void task_stats(const GroupRaw<DT> raw[kTaskGroupsPer
     const double chd = ec.c_hi, cld = ec.c_lo, Ad = A;
 #pragma unroll
     for (int j = 0; j < kTaskGroupsPerLane; ++j) {
+      if (RAGGED && j * 64 * kGroup >= valid) break;
       float v[kGroup];
       unpack<DT>(raw[j], v);
       double e[kGroup];
@@ -471,6 +477,7 @@ __device__ __forceinline__ void task_stats(const GroupRaw<DT> raw[kTaskGroupsPer
   } else {
 #pragma unroll
     for (int j = 0; j < kTaskGroupsPerLane; ++j) {
+      if (RAGGED && j * 64 * kGroup >= valid) break;
       float v[kGroup];
       unpack<DT>(raw[j], v);
       float e[kGroup];
@@ -514,7 +521,9 @@ __global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(
   float m;
   double s;
   uint32_t bad = 0;
-  task_stats<DT, CHECK>(raw, ec, m, s, bad);
+  const int64_t valid = V - chunk * kWaveTaskElems;
+  if (valid >= kWaveTaskElems) task_stats<DT, CHECK, false>(raw, ec, valid, m, s, bad);
+  else task_stats<DT, CHECK, true>(raw, ec, valid, m, s, bad);
   if (CHECK) bad = wave_or(bad);
   if (lane == 0) {
     // a non-temporal 16-byte store: the partial goes out now instead of
