@@ -12,7 +12,7 @@ def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; parity against the oracle")
     config.addinivalue_line(
-        "markers", "slow: CPU test that takes more than a few seconds")
+        "markers", "slow: takes more than a few seconds (CPU pins, the GPU parity sweep)")
 
 
 @pytest.fixture(scope="session")
