@@ -269,8 +269,11 @@ class Bench:
         med_s = step_p["p50"] / 1e6
         k_med = [float(np.median(k)) for k in kern]
         achieved = first / (k_med[0] / 1e6) / 1e9
-        ora, o_times = run_oracle(inp, runs=a.oracle_runs if idx == HEADLINE else 1,
-                                  budget_s=a.cpu_budget if idx == HEADLINE else 0.0)
+        # the oracle's rate is a median over --oracle-runs runs (the headline
+        # repeats until the CPU budget is spent); --cpu-budget 0 times the
+        # other workloads once, from their parity run
+        ora, o_times = run_oracle(inp, runs=a.oracle_runs if (idx == HEADLINE or a.cpu_budget > 0)
+                                  else 1, budget_s=a.cpu_budget if idx == HEADLINE else 0.0)
         o_med = float(np.median(o_times))
         rec = {
             "workload": inp.name, "B": inp.num_seqs,
