@@ -150,13 +150,14 @@ def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
                                      (8, 1_000_000, 3_000_000)])
 def test_workspace_covers_every_row_partial_and_tile(V, B, R_d):
     """The workspace must hold one 16-byte partial per 4096 logits of all
-    R_t + R_d = B + 2 R_d rows the statistics pass reads, one double per
-    2048-logit tile per sequence and one counter per sequence."""
+    R_t + R_d = B + 2 R_d rows the statistics pass reads, four doubles per
+    2048-logit tile per sequence (the residual's tile sums) and one counter
+    per sequence."""
     lib = R.load_library()
     ws = ctypes.c_size_t()
     assert lib.spec_verify_query_workspace(V, B, R_d, ctypes.byref(ws)) == binding.OK
     rows = B + 2 * R_d
-    need = rows * -(-V // 4096) * 16 + B * -(-V // 2048) * 8 + B * 4
+    need = rows * -(-V // 4096) * 16 + B * -(-V // 2048) * 4 * 8 + B * 4
     assert ws.value >= need
     assert ws.value % 256 == 0
     assert lib.spec_verify_query_workspace(0, B, R_d, ctypes.byref(ws)) == binding.EUNSUPPORTED
