@@ -170,7 +170,10 @@ class Bench:
         self.torch = torch
         torch.cuda.set_device(0)
         self.dev = torch.device("cuda", 0)
-        self.stream = torch.cuda.current_stream(self.dev)
+        # every call goes to a stream of its own (default priority), which
+        # is also torch's current stream from here on
+        self.stream = torch.cuda.Stream(self.dev)
+        torch.cuda.set_stream(self.stream)
 
     def events(self, n):
         evs = [self.torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -184,6 +187,22 @@ class Bench:
         if dtype == "bf16":
             return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(self.dev)
         return torch.from_numpy(arr).to(self.dev)
+
+    def spans(self, call):
+        """K steps, each between an event pair of its own on the stream:
+        per-step spans (us) and the wall-clock mean per step (us)."""
+        a = self.a
+        torch = self.torch
+        pairs = [self.events(2) for _ in range(a.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            pairs[i][0].record(self.stream)
+            call(i, None)
+            pairs[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        wall_us = (time.perf_counter() - t0) * 1e6 / a.steps
+        return [e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs], wall_us
 
     def timed(self, call, nk):
         """W untimed steps, then the K timed steps, each between an event
@@ -208,16 +227,7 @@ class Bench:
             self.warmup_run += 1
             if self.warmup_run % 64 == 0:
                 torch.cuda.synchronize()
-        pairs = [self.events(2) for _ in range(a.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(a.steps):
-            pairs[i][0].record(self.stream)
-            call(i, None)
-            pairs[i][1].record(self.stream)
-        torch.cuda.synchronize()
-        wall_us = (time.perf_counter() - t0) * 1e6 / a.steps
-        spans = [e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs]
+        spans, wall_us = self.spans(call)
         ev = [self.events(2 * nk) for _ in range(a.steps)]
         torch.cuda.synchronize()
         for i in range(a.steps):
@@ -288,13 +298,16 @@ class Bench:
         nk = sv.num_kernels
 
         def step(i, events):
-            # torch's current stream: the default stream, or the capture
+            # torch's current stream: the bench's stream, or the capture
             # stream inside graph_step_us
             t, d = sets[i % len(sets)]
             sv(cu, t, d, tok, uni, inp.temperature, out=outs[i % len(sets)],
                stream=torch.cuda.current_stream(self.dev), timing_events=events)
 
         spans, kern, wall_us, plain_us = self.timed(step, nk)
+        # unflushed: the same input set every step, so part of a step's rows
+        # may still be in the Infinity Cache from the step before
+        same, _ = self.spans(lambda i, ev: step(0, ev))
         graph = self.graph_step_us(step) if idx in (1, 2) else None
         torch.cuda.synchronize()
         num_acc = outs[0].num_accepted.cpu().numpy()
@@ -317,6 +330,7 @@ class Bench:
             "target_rows": inp.target_rows, "draft_rows": inp.draft_rows,
             "step_us": step_p, "wall_us_per_step": round(wall_us, 2),
             "unevented_us_per_step": round(plain_us, 2), "warmup_steps_run": self.warmup_run,
+            "unflushed_step_us": pct(same),
             "graph_step_us": graph,
             "verified_rows_per_s": round(inp.target_rows / med_s, 1),
             "hbm_gbps": round(step_bytes / med_s / 1e9, 1),
@@ -583,6 +597,7 @@ def main() -> int:
                    "target_rows": hr["target_rows"], "draft_rows": hr["draft_rows"]},
         "step_us": hr["step_us"], "wall_ms_per_step": round(hr["wall_us_per_step"] / 1e3, 5),
         "unevented_ms_per_step": round(hr["unevented_us_per_step"] / 1e3, 5),
+        "unflushed_step_us": hr["unflushed_step_us"],
         "warmup_steps_run": hr["warmup_steps_run"],
         "sequences_per_s": round(hr["B"] / (med_ms / 1e3), 1),
         "all_rows_per_s": round((hr["target_rows"] + hr["draft_rows"]) / (med_ms / 1e3), 1),
