@@ -70,3 +70,58 @@ def test_static_workspace_capacity_error():
     a.workspace = ctypes.c_void_p(sv.workspace.data_ptr())
     a.workspace_bytes = sv.workspace.numel()
     assert lib.spec_verify_run(sv._ctx, ctypes.byref(a), None) == binding.EINVAL
+
+
+
+def _graph_inputs(k):
+    # one shape for every k (a captured launch has fixed sizes), new values
+    return W.build(f"static graph {k}", 4200 + k, [3, 0, 8, 5, 1, 8, 2, 6], 20000, W.BF16, 0.9,
+                   W.boosted_random_ids_rows(3.0, 20, 8.0), 1.0)
+
+
+def _copy_into(dst, src):
+    for name in ("cu", "target", "draft", "tokens", "uniforms"):
+        getattr(dst, name).copy_(getattr(src, name))
+
+
+def test_static_workspace_replays_in_a_graph():
+    """The callers the entry point is for: spec_verify_run_static captured in
+    a HIP graph and replayed with new inputs copied in between (and eager
+    calls of it between the replays), every replay bit-identical to an eager
+    spec_verify_run on the same inputs."""
+    import torch
+    from tests.gpu_helpers import make_verifier
+    replays = 4
+    log("[static] graph replay")
+    inps = [_graph_inputs(k) for k in range(replays)]
+    sv = make_verifier(inps[0])
+    dev_sets = [to_device(x) for x in inps]
+    B, R_d, T = inps[0].num_seqs, inps[0].draft_rows, inps[0].temperature
+
+    def static(d, out):
+        return sv.run_static(d.cu, d.target, d.draft, d.tokens, d.uniforms, T, out=out)
+
+    eager = []
+    for d in dev_sets:
+        out = sv.allocate_outputs(B, R_d)
+        sv(d.cu, d.target, d.draft, d.tokens, d.uniforms, T, out=out)
+        torch.cuda.synchronize()
+        eager.append(_host(out))
+    cap_in = to_device(inps[0])
+    cap_out = sv.allocate_outputs(B, R_d)
+    static(cap_in, cap_out)                     # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        static(cap_in, cap_out)
+    for rep in range(2 * replays):
+        k = (3 * rep + 1) % replays
+        _copy_into(cap_in, dev_sets[k])
+        g.replay()
+        torch.cuda.synchronize()
+        got = _host(cap_out)
+        for key in FIELDS:
+            assert np.array_equal(got[key], eager[k][key], equal_nan=True), (rep, k, key)
+        static(dev_sets[(k + 1) % replays], sv.allocate_outputs(B, R_d))
+        torch.cuda.synchronize()
+    assert int(cap_out.status.cpu().item()) == 0
