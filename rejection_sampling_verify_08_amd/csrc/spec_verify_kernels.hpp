@@ -643,9 +643,12 @@ struct DrawConsts {
 //   qs = e_q             (q_k in the same scale; dw/dg)
 //   w  = max(0, r0 + g qs)
 // with e_q the draft term moved into the target's scale.  Below |d0| = 1/2
-// r0 = e_p m0 from a polynomial in d0 (relative precision near 0) and qs = e_p - r0;
-// above it both terms are exponentials and their difference keeps at least
-// 29% of its larger term.  -inf logits need no special case: d0 is then
+// r0 = e_p m0 from a polynomial in d0 (relative precision near 0); above it
+// both terms are exponentials and their difference keeps at least 29% of its
+// larger term.  qs is the draft exponential in both ranges (e_p - r0 below
+// 1/2 would equal it up to rounding): it enters w only through g qs, and the
+// exact ratio below needs its sum only to the row sums' precision.  -inf
+// logits need no special case: d0 is then
 // infinite or NaN (the exponential branch) and the exponentials are 0.
 constexpr float kSeriesLimit = 0.5f;
 // (1 - 2^-x) / x on |x| <= 1/2: the degree-5 polynomial that interpolates it
@@ -676,7 +679,7 @@ __device__ __forceinline__ ResidualTerm residual_term(float lp, float lq, const 
   const bool small = __builtin_fabsf(d0) < kSeriesLimit;
   ResidualTerm r;
   r.r0 = small ? ep * (ps * d0) : ep - qx;
-  r.qs = small ? ep - r.r0 : qx;
+  r.qs = qx;
   r.wu = __builtin_fmaf(dc.g, r.qs, r.r0);
   r.w = __builtin_fmaxf(r.wu, 0.0f);     // a NaN (0 - 0 * inf) gives 0
   return r;
@@ -956,7 +959,7 @@ __device__ __forceinline__ int64_t draw_from_task_sums(
 
 constexpr int kTileTerms = 4;                 // W, Q, R0, B per tile
 constexpr double kBand = 0x1p-20;             // |g* - g| / max(1, |g|) the first-order move covers
-constexpr double kCorrectionTol = 0x1p-24;    // band error allowed, relative to W
+constexpr double kCorrectionTol = 0x1p-24;    // error bound allowed, relative to W
 constexpr double kResidualFloor = 0x1p-60;    // residual mass the fp32 terms resolve
 
 // The residual tile pass over tiles [t_lo, t_hi) of one row pair, by the
@@ -968,7 +971,10 @@ constexpr double kResidualFloor = 0x1p-60;    // residual mass the fp32 terms re
 // l+192 (each 16-byte load instruction covers 1 KB of contiguous logits).
 // For every tile, emit(t, v) is called by all lanes of the wave with the
 // tile's sums v = {W, Q, R0, B} (double, equal in every lane); a tile's sums
-// do not depend on the wave that computes them.
+// do not depend on the wave that computes them.  W and R0 cross the lanes in
+// double (the draw and the exact ratio need them to the elements'
+// precision); Q (the slope of the first-order move, ~1e-7 of W at most) and
+// B (an error bound) in float.
 template <int DT, bool VEC, typename Emit>
 __device__ __forceinline__ void residual_tiles(const void* prow, const void* qrow, int64_t V,
                                                int64_t t_lo, int64_t t_hi, const DrawConsts& dc,
@@ -994,7 +1000,9 @@ __device__ __forceinline__ void residual_tiles(const void* prow, const void* qro
         gw += r.w;
         gr += r.r0;
         gq += r.wu > 0.0f ? r.qs : 0.0f;
-        gb += __builtin_fabsf(r.wu) <= band * r.qs ? r.qs : 0.0f;
+        // how far inside the band the element lies: the most its weight
+        // can leave the first-order move for any |g* - g| <= band
+        gb += __builtin_fmaxf(__builtin_fmaf(band, r.qs, -__builtin_fabsf(r.wu)), 0.0f);
       }
       sw += gw;
       sq += gq;
@@ -1003,9 +1011,9 @@ __device__ __forceinline__ void residual_tiles(const void* prow, const void* qro
     }
     double v[kTileTerms];
     v[0] = wave_xor_sum((double)sw);
-    v[1] = wave_xor_sum((double)sq);
+    v[1] = (double)wave_xor_sum(sq);
     v[2] = wave_xor_sum((double)sr);
-    v[3] = wave_xor_sum((double)sb);
+    v[3] = (double)wave_xor_sum(sb);
     emit(t, v);
     int claimed = 0;
     if (lane == 0) claimed = atomicAdd(next, 1);
@@ -1272,9 +1280,9 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
   } else {
     // ---- the residual's tile pass.  Tile sums of this workgroup's share:
     // per tile the weights W (with the row pass's g), the draft terms Q over
-    // the support (dW/dg), the C-free difference R0 and the band mass B of
-    // elements within 2^-20 of the support's edge.  Sums of a lane's 32
-    // elements are fp32, the wave's total is double.  Tile arrays, in LDS:
+    // the support (dW/dg), the C-free difference R0 and the band bound
+    // B = sum max(0, band qs - |wu|) (band = 2^-20 max(1, |g|)).  Sums of a
+    // lane's 32 elements are fp32.  Tile arrays, in LDS:
     // W at tile_sum[0, nt), Q at [nt, 2 nt), R0 at [2 nt, 3 nt), B at
     // [3 nt, 4 nt).
     const int64_t nt = num_tiles;
@@ -1329,9 +1337,10 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     // the rounding of those differences, while the row pass's s_p / s_q is
     // exact only to its sums' rounding (~1e-8): g* = 1 - s_p' / s_q' =
     // -R0 / (s_p' - R0).  W is linear in g for a fixed support, so the tile
-    // sums move by (g* - g) Q; elements whose sign can change lie in the
-    // band (g* - g is checked to be inside it), and their mass bounds the
-    // error.  Waves 0-3 total the four arrays in a fixed order.
+    // sums move by dg Q (dg = g* - g).  An element that changes side is off
+    // by |dg| qs - |wu| at most; max(0, x qs - |wu|) is convex in x and 0 at
+    // x = 0, so for |dg| <= band the total error is at most (|dg| / band) B.
+    // Waves 0-3 total the four arrays in a fixed order.
     if (wave < kTileTerms) {
       const double tot = wave_total(tile_sum + wave * nt, nt, lane);
       if (lane == 0) ds.red[wave] = tot;
@@ -1343,7 +1352,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     const double w_star = ds.red[0] + dg * ds.red[1];
     const double band = kBand * __builtin_fmax(1.0, __builtin_fabs((double)dc.g));
     const bool linear_ok = w_star > 0.0 && __builtin_fabs(dg) <= band &&
-                           2.0 * __builtin_fabs(dg) * ds.red[3] <= kCorrectionTol * w_star;
+                           2.0 * (__builtin_fabs(dg) / band) * ds.red[3] <=
+                               kCorrectionTol * w_star;
     dc.g = g_star;                     // the search below uses g*
     __syncthreads();                   // ds.red is reused
     if (linear_ok) {
