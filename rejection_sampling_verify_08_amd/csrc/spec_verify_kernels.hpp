@@ -890,20 +890,23 @@ __device__ __forceinline__ int64_t draw_from_task_sums(
   const bool point = dc.residual == kDrawPoint;
   const int64_t xtask = point ? dc.x / kWaveTaskElems : -1;
   const bool active = tid < kTaskGroups;
-  // issue the partial loads and the x-task's groups together
+  // A task whose groups are needed whatever the sums say (the x-task, or
+  // the only task of a row of at most 4096 logits) is loaded first, so that
+  // its loads and the partials' are in flight together.
+  const int64_t early = point ? xtask : (tpr == 1 ? 0 : -1);
+  GroupRaw<DT> rp;
+  int64_t gi = early * kTaskGroups + tid;
+  if (early >= 0 && active) load_group<DT, VEC>(prow, gi, V, rp);
   for (int64_t c = tid; c < tpr; c += kThreads) {
     const Partial pc = part[c];
     task_sum[c] = (pc.m == -INFINITY)
                       ? 0.0
                       : pc.s * exp2((double)dc.Ap - (double)shift_of(pc.m, ec));
   }
-  GroupRaw<DT> rp;
-  int64_t gi = xtask * kTaskGroups + tid;
   double xsum = 0.0;
   if (point) {
     double gsum = 0.0;
     if (active) {
-      load_group<DT, VEC>(prow, gi, V, rp);
       float w[kGroup];
       weights_of<DT>(rp, rp, gi * kGroup, dc, ec, w);
       gsum = (double)seq_sum8(w);
@@ -946,7 +949,7 @@ __device__ __forceinline__ int64_t draw_from_task_sums(
   total = ds.total;
   const int64_t tau = ds.tau;
   if (tau < 0) return -1;                      // no mass at all (invalid row)
-  if (tau != xtask) {
+  if (tau != early) {
     gi = tau * kTaskGroups + tid;
     if (active) load_group<DT, VEC>(prow, gi, V, rp);
   }
