@@ -1154,6 +1154,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     if (wave == 0) {
       bool reject = false, badtok = false;
       uint32_t wbad = 0;
+      float p_out = 0.0f, q_out = 0.0f;
       if (i_me < hi_d) {
         double r = 0.0;
         if (x < 0 || x >= V) {
@@ -1162,8 +1163,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
           const double Mp = sh.M[0][lane], sp = sh.s[0][lane];
           // r = p_i(x) / 1
           r = exp(((double)lpx - Mp) / ec.T) / sp;
-          if (g == 0 && out_p) out_p[drow0 + i_me] = (float)r;
-          if (g == 0 && out_q) out_q[drow0 + i_me] = 1.0f;
+          p_out = (float)r;
+          q_out = 1.0f;
           if (CHECK && Mp == -INFINITY) wbad |= SPEC_VERIFY_DEV_EMPTY_ROW;
         } else {
           const double Mp = sh.M[0][lane], Mq = sh.M[1][lane];
@@ -1172,8 +1173,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
           const double pp = exp(((double)lpx - Mp) / ec.T) / sp;
           const double qq = exp(((double)lqx - Mq) / ec.T) / sq;
           r = exp((((double)lpx - Mp) - ((double)lqx - Mq)) / ec.T) * (sq / sp);
-          if (g == 0 && out_p) out_p[drow0 + i_me] = (float)pp;
-          if (g == 0 && out_q) out_q[drow0 + i_me] = (float)qq;
+          p_out = (float)pp;
+          q_out = (float)qq;
           if (CHECK) {
             if (!(qq > 0.0)) wbad |= SPEC_VERIFY_DEV_ZERO_Q;
             if (Mp == -INFINITY || Mq == -INFINITY) wbad |= SPEC_VERIFY_DEV_EMPTY_ROW;
@@ -1185,6 +1186,15 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
       }
       const uint64_t mask = __ballot(reject);
       const uint64_t btok = __ballot(badtok);
+      // p and q go out after the test: loads and stores share one counter,
+      // so a store issued before u's first use makes the wave wait for the
+      // store's round trip there (the scheduling barrier keeps the compiler
+      // from moving the stores above the ballots)
+      __builtin_amdgcn_sched_barrier(0);
+      if (g == 0 && i_me < hi_d && !badtok) {
+        if (out_p) out_p[drow0 + i_me] = p_out;
+        if (out_q) out_q[drow0 + i_me] = q_out;
+      }
       wbad = wave_or(wbad);
       sh.x[lane] = x;
       if (lane == 0) {
