@@ -35,12 +35,12 @@
 //     the first rejection ends the test).  A residual w_k = max(0, p_k - q_k)
 //     needs both rows again: the G workgroups share one more read of the
 //     rejected target/draft pair, formed without cancellation (residual_term),
-//     with four double sums per 2048-logit tile (residual_tiles; the tiles of
-//     a workgroup handed to its waves through an LDS counter), and the last
-//     workgroup to arrive (an integer counter cleared by the row pass) moves
-//     the sums to the exact normaliser ratio and scans them for the tile
-//     holding t = u * S.  A bonus draw
-//     (w_k = p_k) and a point-mass residual (p with x removed) need no
+//     with four sums per 2048-logit tile, kept in double (residual_tiles; the
+//     tiles of a workgroup handed to its waves through an LDS counter), and
+//     the last workgroup to arrive (an integer counter cleared by the row
+//     pass) moves the sums to the exact normaliser ratio and scans them for
+//     the tile holding t = u * S.  A bonus draw (w_k = p_k) and a point-mass
+//     residual (p with x removed) need no
 //     second pass: the row pass's task sums, moved into the draw's scale,
 //     locate the 4096-logit task holding t (the task holding x is summed
 //     again without it).  Either way the workgroup's 512 threads then search
