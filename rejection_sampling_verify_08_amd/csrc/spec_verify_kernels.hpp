@@ -129,7 +129,14 @@ __device__ __forceinline__ double offset_of(float m, float A, const ExpConsts& c
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   // lanes whose source is outside the row, or whose row is masked, get 0
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+  if constexpr (ROW_MASK == 0xF) {
+    // every lane is written (bound_ctrl: an out-of-row source reads as 0),
+    // so no old value has to be set up first
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+  } else {
+    // lanes of masked rows are not written and keep the old value, 0
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+  }
 }
 
 constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
