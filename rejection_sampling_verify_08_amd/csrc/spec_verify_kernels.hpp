@@ -146,6 +146,7 @@ constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within 16
 constexpr int kDppRowShr = 0x110;     // + n: lane i <- i - n within a row of 16
 constexpr int kDppBcast15 = 0x142;    // lane 15 of a row -> the next row
 constexpr int kDppBcast31 = 0x143;    // lane 31 -> rows 2 and 3
+constexpr int kDppWaveShr1 = 0x138;   // lane i <- i - 1 across the wave (lane 0 gets 0)
 
 template <typename T>
 struct LaneBits;
@@ -768,11 +769,10 @@ __device__ __forceinline__ void find_interval(const double* v, int64_t n, double
     const double x = (c + lane < n) ? v[c + lane] : 0.0;
     const double incl = base + wave_incl_scan(x, lane);
     const uint64_t hit = __ballot(c + lane < n && incl > tt);
-    const double below = __shfl_up(incl, 1);
     if (hit) {
       const int l = __builtin_ctzll(hit);
       tau = c + l;
-      p_excl = lane_value(lane == 0 ? base : below, l);
+      p_excl = l == 0 ? base : lane_value(incl, l - 1);
     }
     base = lane_value(incl, 63);
   }
@@ -813,7 +813,7 @@ __device__ __forceinline__ int64_t block_search_weights(const float w[kGroup], i
   const int wave = tid >> 6;
   const double gs = (double)seq_sum8(w);
   const double incl = wave_incl_scan(gs, lane);
-  const double below = __shfl_up(incl, 1);
+  const double below = LaneBits<double>::dpp<kDppWaveShr1>(incl);   // lane - 1's, 0 in lane 0
   if (lane == 63) ds.wave_tot[wave] = incl;
   __syncthreads();
   double base = p_excl;
