@@ -257,8 +257,10 @@ struct OpOr {
 struct OpMax {   // maximum that ignores NaN operands
   __device__ float operator()(float a, float b) const { return fmax_nan_ignoring(a, b); }
 };
-struct OpMaxI64 {
-  __device__ int64_t operator()(int64_t a, int64_t b) const { return a > b ? a : b; }
+struct OpMaxI32 {   // signed maximum of 32-bit values carried as uint32_t
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
+    return (int32_t)a > (int32_t)b ? a : b;
+  }
 };
 
 template <typename T>
@@ -739,8 +741,8 @@ struct SeqShared {
 
 struct DrawShared {
   double wave_tot[kWaves];   // block scan: per-wave group-sum totals
-  int64_t cand[kWaves];      // block search: per-wave first hit (or -1)
-  int64_t last_pos[kWaves];  // block search: per-wave last positive weight
+  int32_t cand[kWaves];      // block search: per-wave first hit (or -1)
+  int32_t last_pos[kWaves];  // block search: per-wave last positive weight
   double red[kWaves];        // block reduction
   double total, tt, p_excl;  // the draw's total, u * total, mass before tau
   int64_t tau;               // the tile / task holding tt
@@ -819,33 +821,35 @@ __device__ __forceinline__ int64_t block_search_weights(const float w[kGroup], i
   double base = p_excl;
   for (int v = 0; v < wave; ++v) base += ds.wave_tot[v];
   const double excl = lane == 0 ? 0.0 : below;
+  // logit indices fit 32 bits (V <= kMaxVocab)
   int k_hit = -1;
-  int64_t last_pos = -1;
+  int32_t last_pos = -1;
   float c = 0.0f;
 #pragma unroll
   for (int k = 0; k < kGroup; ++k) {
     c += w[k];
     if (k_hit < 0 && w[k] > 0.0f && base + (excl + (double)c) > tt) k_hit = k;
-    if (w[k] > 0.0f) last_pos = gi * kGroup + k;
+    if (w[k] > 0.0f) last_pos = (int32_t)(gi * kGroup + k);
   }
   const uint64_t hit = __ballot(k_hit >= 0);
-  int64_t cand = -1;
+  int32_t cand = -1;
   if (hit) {
     const int l = __builtin_ctzll(hit);
-    cand = (gi - lane + l) * kGroup + (int)lane_value((uint32_t)k_hit, l);
+    cand = (int32_t)((gi - lane + l) * kGroup) + (int32_t)lane_value((uint32_t)k_hit, l);
   }
-  last_pos = group_reduce(last_pos, 64, OpMaxI64());
+  last_pos = (int32_t)group_reduce((uint32_t)last_pos, 64, OpMaxI32());
   if (lane == 0) {
     ds.cand[wave] = cand;
     ds.last_pos[wave] = last_pos;
   }
   __syncthreads();
-  int64_t token = -1, lp = -1;
-  for (int v = 0; v < kWaves; ++v) {
-    if (token < 0 && ds.cand[v] >= 0) token = ds.cand[v];
-    lp = ds.last_pos[v] > lp ? ds.last_pos[v] : lp;
-  }
-  return token >= 0 ? token : lp;
+  // the first wave with a hit (lanes 0..kWaves-1 read one wave's result
+  // each), else the last positive weight of the interval
+  const int32_t cv = lane < kWaves ? ds.cand[lane] : -1;
+  const uint64_t hits = __ballot(cv >= 0);
+  if (hits) return (int32_t)lane_value((uint32_t)cv, __builtin_ctzll(hits));
+  const int32_t lv = lane < kWaves ? ds.last_pos[lane] : -1;
+  return (int32_t)lane_value(group_reduce((uint32_t)lv, kWaves, OpMaxI32()), 0);
 }
 
 template <int DT>
