@@ -746,6 +746,9 @@ struct DrawShared {
   double red[kWaves];        // block reduction
   double total, tt, p_excl;  // the draw's total, u * total, mass before tau
   int64_t tau;               // the tile / task holding tt
+  double dg;                 // residual: the first-order move g* - g
+  float g_star;              // residual: the exact normaliser ratio
+  int linear_ok;             // residual: the move is certified
   int empty;                 // the residual summed to 0
   int last_wg;               // this workgroup arrived last
 };
@@ -1348,13 +1351,16 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
       }
       __syncthreads();
       if (!ds.last_wg) return;
-      // the last workgroup copies the tile sums into its LDS
-      for (int64_t i = tid; i < nt * kTileTerms; i += kThreads) {
-        const int64_t t = i / kTileTerms, k = i - t * kTileTerms;
-        tile_sum[k * nt + t] =
-            __hip_atomic_load(&ts_seq[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // the last workgroup copies the tile sums into its LDS (a row of at
+      // most 64 tiles: wave 0 loads them into registers below)
+      if (nt > 64) {
+        for (int64_t i = tid; i < nt * kTileTerms; i += kThreads) {
+          const int64_t t = i / kTileTerms, k = i - t * kTileTerms;
+          tile_sum[k * nt + t] =
+              __hip_atomic_load(&ts_seq[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
     // ---- the exact normaliser ratio.  R0 = s_p' - s_q' (both in the
     // weights' scale) comes from per-element differences, so it is exact to
@@ -1364,54 +1370,118 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     // sums move by dg Q (dg = g* - g).  An element that changes side is off
     // by |dg| qs - |wu| at most; max(0, x qs - |wu|) is convex in x and 0 at
     // x = 0, so for |dg| <= band the total error is at most (|dg| / band) B.
-    // Waves 0-3 total the four arrays in a fixed order.
-    if (wave < kTileTerms) {
-      const double tot = wave_total(tile_sum + wave * nt, nt, lane);
-      if (lane == 0) ds.red[wave] = tot;
-    }
-    __syncthreads();
-    const double R0 = ds.red[2];
-    const float g_star = (float)(-R0 / (unit - R0));
-    const double dg = (double)g_star - (double)dc.g;
-    const double w_star = ds.red[0] + dg * ds.red[1];
+    // The four totals are scans in a fixed order (wave_total's).  Then,
+    // with the move certified, the moved tile sums are scanned for the tile
+    // holding t = u * S; an empty residual (invalid input or extreme
+    // rounding) falls back to a draw from p_n through the task sums.
     const double band = kBand * __builtin_fmax(1.0, __builtin_fabs((double)dc.g));
-    const bool linear_ok = w_star > 0.0 && __builtin_fabs(dg) <= band &&
-                           2.0 * (__builtin_fabs(dg) / band) * ds.red[3] <=
-                               kCorrectionTol * w_star;
-    dc.g = g_star;                     // the search below uses g*
-    __syncthreads();                   // ds.red is reused
-    if (linear_ok) {
-      for (int64_t t = tid; t < nt; t += kThreads) {
-        const double c = tile_sum[t] + dg * tile_sum[nt + t];
-        tile_sum[t] = c > 0.0 ? c : 0.0;
-      }
-    } else {
-      // the support moves with g: this workgroup passes over both rows again
-      // with g* (rare: rows that agree to the row pass's rounding)
-      if (tid == 0) sh.tile_next = 0;
-      __syncthreads();
-      residual_tiles<DT, VEC>(prow, qrow, V, 0, nt, dc, ec, &sh.tile_next,
-                              [&](int64_t t, const double v[kTileTerms]) {
-        if (lane == 0) tile_sum[t] = v[0];
-      });
-    }
-    __syncthreads();
-    // ---- wave 0 scans the tile sums in order and finds the tile holding
-    // t = u * S; an empty residual (invalid input or extreme rounding) falls
-    // back to a draw from p_n through the task sums.
-    if (wave == 0) {
-      double tt = 0.0;
-      total = wave_total(tile_sum, nt, lane);
-      if (total > 0.0) {
-        tt = (double)u_final * total;
-        find_interval(tile_sum, nt, tt, lane, ds);
-      }
+    // from the four totals: g*, the move dg and whether it is certified,
+    // also left in ds (lane 0) for the other waves
+    auto certify = [&](double W, double Q, double R0, double B, double& dg) -> bool {
+      const float g_star = (float)(-R0 / (unit - R0));
+      dg = (double)g_star - (double)dc.g;
+      const double w_star = W + dg * Q;
+      const bool ok = w_star > 0.0 && __builtin_fabs(dg) <= band &&
+                      2.0 * (__builtin_fabs(dg) / band) * B <= kCorrectionTol * w_star;
       if (lane == 0) {
-        ds.total = total;
-        ds.tt = tt;
+        ds.g_star = g_star;
+        ds.dg = dg;
+        ds.linear_ok = ok ? 1 : 0;
+      }
+      return ok;
+    };
+    bool scanned = false;
+    if (nt <= 64) {
+      // One wave holds every tile (lane t: tile t) and does the totals, the
+      // move and the scan in registers, without a workgroup barrier.
+      if (wave == 0) {
+        double v[kTileTerms] = {0.0, 0.0, 0.0, 0.0};
+        if (lane < nt) {
+#pragma unroll
+          for (int k = 0; k < kTileTerms; ++k)
+            v[k] = G > 1 ? __hip_atomic_load(&ts_seq[lane * kTileTerms + k], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
+                         : tile_sum[k * nt + lane];
+        }
+        double tot[kTileTerms];
+#pragma unroll
+        for (int k = 0; k < kTileTerms; ++k) tot[k] = lane_value(wave_incl_scan(v[k], lane), 63);
+        double dg;
+        if (certify(tot[0], tot[1], tot[2], tot[3], dg)) {
+          double c = v[0] + dg * v[1];
+          c = c > 0.0 ? c : 0.0;
+          if (lane < nt) tile_sum[lane] = c;
+          const double incl = wave_incl_scan(c, lane);
+          const double sum = lane_value(incl, 63);
+          double tt = 0.0;
+          if (sum > 0.0) {
+            tt = (double)u_final * sum;
+            const uint64_t hit = __ballot(lane < nt && incl > tt);
+            if (hit) {
+              const int l = __builtin_ctzll(hit);
+              const double p_excl = l == 0 ? 0.0 : lane_value(incl, l - 1);
+              if (lane == 0) {
+                ds.tau = l;
+                ds.p_excl = p_excl;
+              }
+            } else {
+              find_interval(tile_sum, nt, tt, lane, ds);   // t past the rounded total
+            }
+          }
+          if (lane == 0) {
+            ds.total = sum;
+            ds.tt = tt;
+          }
+        }
+      }
+      __syncthreads();
+      scanned = ds.linear_ok != 0;
+    } else {
+      if (wave < kTileTerms) {
+        const double tot = wave_total(tile_sum + wave * nt, nt, lane);
+        if (lane == 0) ds.red[wave] = tot;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        double dg;
+        certify(ds.red[0], ds.red[1], ds.red[2], ds.red[3], dg);
+      }
+      __syncthreads();
+      if (ds.linear_ok) {
+        const double dg = ds.dg;
+        for (int64_t t = tid; t < nt; t += kThreads) {
+          const double c = tile_sum[t] + dg * tile_sum[nt + t];
+          tile_sum[t] = c > 0.0 ? c : 0.0;
+        }
       }
     }
-    __syncthreads();
+    dc.g = ds.g_star;                  // the search below uses g*
+    if (!scanned) {
+      if (!ds.linear_ok) {
+        // the support moves with g: this workgroup passes over both rows
+        // again with g* (rare: rows that agree to the row pass's rounding)
+        if (tid == 0) sh.tile_next = 0;
+        __syncthreads();
+        residual_tiles<DT, VEC>(prow, qrow, V, 0, nt, dc, ec, &sh.tile_next,
+                                [&](int64_t t, const double v[kTileTerms]) {
+          if (lane == 0) tile_sum[t] = v[0];
+        });
+      }
+      __syncthreads();
+      if (wave == 0) {
+        double tt = 0.0;
+        total = wave_total(tile_sum, nt, lane);
+        if (total > 0.0) {
+          tt = (double)u_final * total;
+          find_interval(tile_sum, nt, tt, lane, ds);
+        }
+        if (lane == 0) {
+          ds.total = total;
+          ds.tt = tt;
+        }
+      }
+      __syncthreads();
+    }
     total = ds.total;
     if (!(total > 0.0)) {
       fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
