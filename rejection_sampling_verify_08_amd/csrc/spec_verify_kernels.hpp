@@ -1235,12 +1235,15 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
   }
 
   // ---- emit the accepted prefix ([B] 流程编排: keep the drafts before the
-  // first mismatch); slot n is written by the draw below.
-  // The last window's drafts are in LDS; earlier windows (gamma > 64 only)
-  // are read again.
+  // first mismatch); slot n is written by the draw below.  n lies in the
+  // last window [lo, lo + 64), whose drafts are in LDS; drafts of earlier
+  // windows (gamma > 64 only) are read again.  Two loops, so that neither
+  // reads through a pointer that may be LDS or global memory (a generic
+  // load would make the stores wait for every store issued before them).
   if (g == 0) {
-    for (int64_t i = tid; i <= gamma; i += kThreads) {
-      if (i < n) out_tokens[trow0 + i] = i >= lo ? sh.x[i - lo] : tokens[drow0 + i];
+    for (int64_t i = tid; i < lo; i += kThreads) out_tokens[trow0 + i] = tokens[drow0 + i];
+    for (int64_t i = lo + tid; i <= gamma; i += kThreads) {
+      if (i < n) out_tokens[trow0 + i] = sh.x[i - lo];
       else if (i > n) out_tokens[trow0 + i] = -1;
     }
     if (tid == 0) out_num_accepted[b] = (int32_t)n;
