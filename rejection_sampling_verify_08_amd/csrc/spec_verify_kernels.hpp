@@ -911,12 +911,18 @@ __device__ __forceinline__ int64_t draw_from_task_sums(
   GroupRaw<DT> rp;
   int64_t gi = early * kTaskGroups + tid;
   if (early >= 0 && active) load_group<DT, VEC>(prow, gi, V, rp);
-  for (int64_t c = tid; c < tpr; c += kThreads) {
-    const Partial pc = part[c];
-    task_sum[c] = (pc.m == -INFINITY)
-                      ? 0.0
-                      : pc.s * exp2((double)dc.Ap - (double)shift_of(pc.m, ec));
-  }
+  // A row of at most 64 tasks: wave 0 holds every task sum (lane c: task c)
+  // and does the x-task's substitution, the total and the scan for t in
+  // registers, with one workgroup barrier (the scans keep wave_total's and
+  // find_interval's order).  Longer rows go through LDS.
+  const bool one_wave = tpr <= 64;
+  auto task_term = [&](const Partial& pc) {
+    return (pc.m == -INFINITY) ? 0.0 : pc.s * exp2((double)dc.Ap - (double)shift_of(pc.m, ec));
+  };
+  Partial pl;
+  if (one_wave && wave == 0 && lane < tpr) pl = part[lane];
+  if (!one_wave)
+    for (int64_t c = tid; c < tpr; c += kThreads) task_sum[c] = task_term(part[c]);
   double xsum = 0.0;
   if (point) {
     double gsum = 0.0;
@@ -927,39 +933,79 @@ __device__ __forceinline__ int64_t draw_from_task_sums(
     }
     xsum = block_sum(gsum, ds);                   // has a barrier
   }
-  __syncthreads();
-  double xtask_bonus = 0.0;
-  if (point && tid == 0) {
-    xtask_bonus = task_sum[xtask];
-    task_sum[xtask] = xsum;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const double tot = wave_total(task_sum, tpr, lane);
-    if (lane == 0) {
-      ds.total = tot;
-      ds.empty = point && !(tot > 0.0);
+  if (one_wave) {
+    if (wave == 0) {
+      double ts = lane < tpr ? task_term(pl) : 0.0;
+      const double ts_bonus = ts;
+      if (point && lane == xtask) ts = xsum;
+      double incl = wave_incl_scan(ts, lane);
+      double tot = lane_value(incl, 63);
+      const bool empty = point && !(tot > 0.0);
+      if (empty) {   // draw from p: the x-task's own sum again
+        ts = ts_bonus;
+        incl = wave_incl_scan(ts, lane);
+        tot = lane_value(incl, 63);
+      }
+      if (lane < tpr) task_sum[lane] = ts;
+      const double tt = (double)u_final * tot;
+      const uint64_t hit = __ballot(lane < tpr && incl > tt);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        const double p_excl = l == 0 ? 0.0 : lane_value(incl, l - 1);
+        if (lane == 0) {
+          ds.tau = l;
+          ds.p_excl = p_excl;
+        }
+      } else {
+        find_interval(task_sum, tpr, tt, lane, ds);   // t past the rounded total, or no mass
+      }
+      if (lane == 0) {
+        ds.total = tot;
+        ds.empty = empty ? 1 : 0;
+        ds.tt = tt;
+      }
     }
-  }
-  __syncthreads();
-  if (ds.empty) {
-    // empty residual (invalid input or extreme rounding): draw from p
-    fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
-    dc.residual = kDrawBonus;
-    if (tid == 0) task_sum[xtask] = xtask_bonus;
+    __syncthreads();
+    if (ds.empty) {
+      // empty residual (invalid input or extreme rounding): draw from p
+      fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
+      dc.residual = kDrawBonus;
+    }
+  } else {
+    __syncthreads();
+    double xtask_bonus = 0.0;
+    if (point && tid == 0) {
+      xtask_bonus = task_sum[xtask];
+      task_sum[xtask] = xsum;
+    }
     __syncthreads();
     if (wave == 0) {
       const double tot = wave_total(task_sum, tpr, lane);
-      if (lane == 0) ds.total = tot;
+      if (lane == 0) {
+        ds.total = tot;
+        ds.empty = point && !(tot > 0.0);
+      }
+    }
+    __syncthreads();
+    if (ds.empty) {
+      // empty residual (invalid input or extreme rounding): draw from p
+      fbad |= SPEC_VERIFY_DEV_EMPTY_RESIDUAL;
+      dc.residual = kDrawBonus;
+      if (tid == 0) task_sum[xtask] = xtask_bonus;
+      __syncthreads();
+      if (wave == 0) {
+        const double tot = wave_total(task_sum, tpr, lane);
+        if (lane == 0) ds.total = tot;
+      }
+      __syncthreads();
+    }
+    if (wave == 0) {
+      const double tt = (double)u_final * ds.total;
+      find_interval(task_sum, tpr, tt, lane, ds);
+      if (lane == 0) ds.tt = tt;
     }
     __syncthreads();
   }
-  if (wave == 0) {
-    const double tt = (double)u_final * ds.total;
-    find_interval(task_sum, tpr, tt, lane, ds);
-    if (lane == 0) ds.tt = tt;
-  }
-  __syncthreads();
   total = ds.total;
   const int64_t tau = ds.tau;
   if (tau < 0) return -1;                      // no mass at all (invalid row)
