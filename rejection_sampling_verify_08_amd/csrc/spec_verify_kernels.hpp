@@ -1038,39 +1038,67 @@ constexpr double kResidualFloor = 0x1p-60;    // residual mass the fp32 terms re
 // double (the draw and the exact ratio need them to the elements'
 // precision); Q (the slope of the first-order move, ~1e-7 of W at most) and
 // B (an error bound) in float.
+// The four per-lane sums of one tile from its raw groups (see residual_tiles).
+template <int DT>
+__device__ __forceinline__ void tile_terms(const GroupRaw<DT> cp[kTileGroupsPerLane],
+                                           const GroupRaw<DT> cq[kTileGroupsPerLane],
+                                           const DrawConsts& dc, const ExpConsts& ec, float band,
+                                           float& sw, float& sq, float& sr, float& sb) {
+  sw = 0.0f; sq = 0.0f; sr = 0.0f; sb = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kTileGroupsPerLane; ++j) {
+    float lp[kGroup], lq[kGroup];
+    unpack<DT>(cp[j], lp);
+    unpack<DT>(cq[j], lq);
+    float gw = 0.0f, gq = 0.0f, gr = 0.0f, gb = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const ResidualTerm r = residual_term(lp[k], lq[k], dc, ec);
+      gw += r.w;
+      gr += r.r0;
+      gq += r.wu > 0.0f ? r.qs : 0.0f;
+      // how far inside the band the element lies: the most its weight
+      // can leave the first-order move for any |g* - g| <= band
+      gb += __builtin_fmaxf(__builtin_fmaf(band, r.qs, -__builtin_fabsf(r.wu)), 0.0f);
+    }
+    sw += gw;
+    sq += gq;
+    sr += gr;
+    sb += gb;
+  }
+}
+
 template <int DT, bool VEC, typename Emit>
 __device__ __forceinline__ void residual_tiles(const void* prow, const void* qrow, int64_t V,
                                                int64_t t_lo, int64_t t_hi, const DrawConsts& dc,
                                                const ExpConsts& ec, int* next, Emit emit) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // t is wave-uniform and kept in scalar registers, so that the test for a
+  // whole tile below is a branch of the wave, not of its lanes
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // the band scales with g: g's own rounding error is relative
   const float band = (float)kBand * __builtin_fmaxf(1.0f, __builtin_fabsf(dc.g));
   for (int64_t t = t_lo + wave; t < t_hi;) {
     GroupRaw<DT> cp[kTileGroupsPerLane], cq[kTileGroupsPerLane];
-    load_tile<DT, VEC>(prow, t, V, lane, cp);
-    load_tile<DT, VEC>(qrow, t, V, lane, cq);
-    float sw = 0.0f, sq = 0.0f, sr = 0.0f, sb = 0.0f;
+    float sw, sq, sr, sb;
+    if (VEC && (t + 1) * kTileElems <= V) {
+      // a whole tile: the two rows' loads alternate group by group, and the
+      // arithmetic of a group waits only for that group's two loads (a
+      // shared path with the ragged loads below waits for all eight)
+      const int64_t g0 = t * kTileGroups + lane;
 #pragma unroll
-    for (int j = 0; j < kTileGroupsPerLane; ++j) {
-      float lp[kGroup], lq[kGroup];
-      unpack<DT>(cp[j], lp);
-      unpack<DT>(cq[j], lq);
-      float gw = 0.0f, gq = 0.0f, gr = 0.0f, gb = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kGroup; ++k) {
-        const ResidualTerm r = residual_term(lp[k], lq[k], dc, ec);
-        gw += r.w;
-        gr += r.r0;
-        gq += r.wu > 0.0f ? r.qs : 0.0f;
-        // how far inside the band the element lies: the most its weight
-        // can leave the first-order move for any |g* - g| <= band
-        gb += __builtin_fmaxf(__builtin_fmaf(band, r.qs, -__builtin_fabsf(r.wu)), 0.0f);
+      for (int j = 0; j < kTileGroupsPerLane; ++j) {
+        load_full_nt<DT>(prow, (g0 + j * 64) * kGroup, cp[j]);
+        load_full_nt<DT>(qrow, (g0 + j * 64) * kGroup, cq[j]);
       }
-      sw += gw;
-      sq += gq;
-      sr += gr;
-      sb += gb;
+      tile_terms<DT>(cp, cq, dc, ec, band, sw, sq, sr, sb);
+      // keeps the compiler from merging this copy of the arithmetic with the
+      // ragged path's below, which would bring back the wait for all loads
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      load_tile<DT, VEC>(prow, t, V, lane, cp);
+      load_tile<DT, VEC>(qrow, t, V, lane, cq);
+      tile_terms<DT>(cp, cq, dc, ec, band, sw, sq, sr, sb);
     }
     double v[kTileTerms];
     v[0] = wave_xor_sum((double)sw);
