@@ -1044,27 +1044,32 @@ __device__ __forceinline__ void tile_terms(const GroupRaw<DT> cp[kTileGroupsPerL
                                            const GroupRaw<DT> cq[kTileGroupsPerLane],
                                            const DrawConsts& dc, const ExpConsts& ec, float band,
                                            float& sw, float& sq, float& sr, float& sb) {
-  sw = 0.0f; sq = 0.0f; sr = 0.0f; sb = 0.0f;
+  // every sum starts from its first term, not from 0 + term (an addition
+  // the compiler must keep, for the sign of a zero term)
 #pragma unroll
   for (int j = 0; j < kTileGroupsPerLane; ++j) {
     float lp[kGroup], lq[kGroup];
     unpack<DT>(cp[j], lp);
     unpack<DT>(cq[j], lq);
-    float gw = 0.0f, gq = 0.0f, gr = 0.0f, gb = 0.0f;
+    float gw, gq, gr, gb;
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
       const ResidualTerm r = residual_term(lp[k], lq[k], dc, ec);
-      gw += r.w;
-      gr += r.r0;
-      gq += r.wu > 0.0f ? r.qs : 0.0f;
+      const float q = r.wu > 0.0f ? r.qs : 0.0f;
       // how far inside the band the element lies: the most its weight
       // can leave the first-order move for any |g* - g| <= band
-      gb += __builtin_fmaxf(__builtin_fmaf(band, r.qs, -__builtin_fabsf(r.wu)), 0.0f);
+      const float bk = __builtin_fmaxf(__builtin_fmaf(band, r.qs, -__builtin_fabsf(r.wu)), 0.0f);
+      if (k == 0) {
+        gw = r.w; gr = r.r0; gq = q; gb = bk;
+      } else {
+        gw += r.w; gr += r.r0; gq += q; gb += bk;
+      }
     }
-    sw += gw;
-    sq += gq;
-    sr += gr;
-    sb += gb;
+    if (j == 0) {
+      sw = gw; sq = gq; sr = gr; sb = gb;
+    } else {
+      sw += gw; sq += gq; sr += gr; sb += gb;
+    }
   }
 }
 
