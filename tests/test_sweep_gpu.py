@@ -13,10 +13,16 @@ test (tests/gpu_helpers.py):
   spec_verify_run_point_drafts;
 * shapes: vocabulary, batch, ragged gamma (up to 20), dtype, temperature,
   generator, draft noise and row pitch, as test_random_configurations but
-  over further seeds.
+  over further seeds;
+* large: vocabularies of 131073 to 700000 logits (rows of more than 64
+  residual tiles, and above 262144 of more than 64 row-pass tasks: the
+  workgroup-wide scans instead of the one-wave ones), B <= 5, near-identical
+  to distant draft rows, through spec_verify_run and
+  spec_verify_run_point_drafts.
 
-Sizes are capped (V < 9000, B < 25) so that the oracle finishes each case in
-well under a second; each case prints its family, seed and shape first.
+Sizes are capped (V < 9000 and B < 25, or B <= 5 for the large family) so
+that the oracle finishes each case in well under a second; each case prints
+its family, seed and shape first.
 """
 import numpy as np
 import pytest
@@ -87,6 +93,18 @@ def _shapes(seed):
     return inp, V + int(rng.integers(0, 3)) * 8
 
 
+def _large(seed):
+    rng = np.random.default_rng(900_000 + seed)
+    V = int(rng.integers(131_073, 700_000))
+    B = int(rng.integers(1, 6))
+    gam = rng.integers(0, 9, size=B)
+    dtype = W.BF16 if seed % 2 else W.F32
+    T = float(rng.choice([0.2, 0.7, 1.0, 2.0]))
+    gen = _gens(rng, V)[int(rng.integers(0, 3))]
+    return W.build(f"sweep large {seed}", 910_000 + seed, gam, V, dtype, T, gen,
+                   float(rng.choice([0.005, 0.5, 1.5])))
+
+
 def _run(inp, label, point=False, ld=None):
     log(f"[case] {label}: B={inp.num_seqs} R_d={inp.draft_rows} V={inp.vocab} {inp.dtype} "
         f"T={inp.temperature:.4f}")
@@ -115,3 +133,11 @@ def test_sweep_shapes(block):
     for seed in range(block * BLOCK, (block + 1) * BLOCK):
         inp, ld = _shapes(seed)
         _run(inp, f"sweep shapes {seed} ld={ld}", ld=ld)
+
+
+@pytest.mark.parametrize("block", range(3))
+def test_sweep_large_vocabulary(block):
+    for seed in range(block * BLOCK, (block + 1) * BLOCK):
+        inp = _large(seed)
+        _run(inp, f"sweep large {seed}")
+        _run(inp, f"sweep large {seed} point", point=True)
